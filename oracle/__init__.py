@@ -1,0 +1,23 @@
+"""CPU oracle for the TQ2_0_g128 ternary matmul (test infrastructure only).
+
+Imported by ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py``; never by the GPU library or its Python binding.
+"""
+
+from .tq2_oracle import (  # noqa: F401
+    BLOCK_BYTES,
+    BLOCK_WEIGHTS,
+    CODE_VALUE,
+    aos_bytes,
+    code_of,
+    dequantize,
+    dequantize_block_scalar,
+    dequantize_scalar,
+    error_scale,
+    f16_bits_to_float,
+    f16_bits_to_float_array,
+    matmul,
+    matmul_entries,
+    matmul_rows,
+    matmul_scalar,
+)
