@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the TQ2_0_g128 ternary matmul on one MI355X.
+
+Headline (one JSON line on stdout): the decode GEMV M=1, K=N=4096 with the
+fused residual (out = residual + x . W^T), one ``tq2_gemv`` call per step,
+as achieved HBM GB/s of algorithmic bytes (codes + scales + x + residual +
+out, each counted once).  The weight of every call comes from a pool of
+copies larger than the 256 MB Infinity Cache, so each call streams its
+weight from HBM; the calls are replayed back to back from a HIP graph.
+
+Also reported in the same line: the roofline object of the dominant kernel,
+the CPU oracle's throughput on a bounded sample of the same workload, and the
+large-M GEMM (M=1536, K=N=3072) in TFLOP/s against the f16 matrix-core peak.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, 8 TB/s
+F16_MFMA_PEAK_TFLOPS = 2516.6    # MI355X dense f16 matrix-core peak (256 CU, 2.4 GHz)
+METRIC = "TQ2 GEMV achieved HBM GB/s (M=1); TQ2 GEMM TFLOP/s at M=1536 (% roofline)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=4096)
+    p.add_argument("--warmup", type=int, default=512)
+    p.add_argument("--pool-mib", type=int, default=1100,
+                   help="total size of the rotated weight copies (>> 256 MB Infinity Cache)")
+    p.add_argument("--gemm-reps", type=int, default=200)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-gemm", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def gemv_bytes(n, k, residual):
+    codes_scales = n * (k // 128) * 34
+    return codes_scales + 4 * k + 4 * n + (4 * n if residual else 0)
+
+
+def time_graph(torch, graph, replays, stream):
+    """Replay a captured graph ``replays`` times between two events on the
+    stream the kernels run on; returns (event ms, wall s)."""
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end), wall
+
+
+def capture(torch, stream, fn, count):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn(0)                                    # one eager call before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(count):
+                fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def cpu_baseline(case, seconds):
+    """The oracle as it stands, on the host, single BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    import oracle
+    n, k = case["n"], case["k"]
+    nbytes = gemv_bytes(n, k, case["residual"] is not None)
+    with threadpool_limits(limits=1):
+        oracle.matmul(case["aos"], case["x"], n, k, case["residual"])    # warm
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            oracle.matmul(case["aos"], case["x"], n, k, case["residual"])
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full oracle evaluations of the K=N=4096 residual GEMV (float64 numpy "
+                      "dequantize + product, 1 BLAS thread), %.3f s each" % (reps, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
+              "(run with --gpus 1)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import tq2_inputs as G
+    from gemv_tq2_g128_amd import tq2
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(dev)
+
+    # ---- decode GEMV, K = N = 4096, fused residual -------------------------
+    case = G.config2(with_residual=True)
+    n, k = case["n"], case["k"]
+    nbytes = gemv_bytes(n, k, True)
+    aos = torch.from_numpy(case["aos"]).to(dev)
+    soa0 = tq2.reformat_aos_to_soa(aos, n, k)
+    sb = tq2.soa_bytes(n, k)
+    pool = max(1, int(math.ceil(args.pool_mib * 2 ** 20 / sb)))
+    pool_buf = soa0.repeat(pool)                       # pool copies, sb bytes apart
+    x = torch.from_numpy(case["x"]).to(dev).reshape(-1)
+    res = torch.from_numpy(case["residual"]).to(dev).reshape(-1)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    base = pool_buf.data_ptr()
+
+    def gemv_call(i):
+        st = tq2.gemv_ptr(base + (i % pool) * sb, x.data_ptr(), res.data_ptr(), out.data_ptr(),
+                          n, k, torch.cuda.current_stream(dev).cuda_stream)
+        if st != 0:
+            raise RuntimeError("tq2_gemv failed: %s" % tq2.status_string(st))
+
+    graph = capture(torch, stream, gemv_call, pool)
+    time_graph(torch, graph, max(1, args.warmup // pool), stream)
+    replays = max(1, int(math.ceil(args.steps / pool)))
+    steps = replays * pool
+    ms, wall = time_graph(torch, graph, replays, stream)
+    us_per_call = ms * 1e3 / steps
+    gbs = nbytes / (us_per_call * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": max(1, args.warmup // pool) * pool,
+        "ms_per_step": round(ms / steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV M=1 K=4096 N=4096 with fused residual; weight "
+                               "rotated over %d copies (%.0f MiB) so every call reads HBM; "
+                               "calls replayed back to back from a HIP graph" %
+                               (pool, pool * sb / 2 ** 20),
+                   "m": 1, "n": n, "k": k, "bytes_per_call": nbytes,
+                   "wall_s_timed": round(wall, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_kernel", "us_per_launch": round(us_per_call, 3)},
+    }
+
+    # ---- large-M GEMM, M = 1536, K = N = 3072 --------------------------------
+    if not args.no_gemm:
+        c4 = G.config4()
+        m4, n4, k4 = c4["m"], c4["n"], c4["k"]
+        soa4 = tq2.reformat_aos_to_soa(torch.from_numpy(c4["aos"]).to(dev), n4, k4)
+        x4 = torch.from_numpy(c4["x"]).to(dev)
+        out4 = torch.empty((m4, n4), dtype=torch.float32, device=dev)
+
+        def gemm_call(i):
+            st = tq2.gemm_ptr(soa4.data_ptr(), x4.data_ptr(), 0, out4.data_ptr(), m4, n4, k4,
+                              torch.cuda.current_stream(dev).cuda_stream)
+            if st != 0:
+                raise RuntimeError("tq2_gemm failed: %s" % tq2.status_string(st))
+
+        per_graph = 20
+        g4 = capture(torch, stream, gemm_call, per_graph)
+        time_graph(torch, g4, 2, stream)
+        reps = max(1, args.gemm_reps // per_graph)
+        ms4, _ = time_graph(torch, g4, reps, stream)
+        us4 = ms4 * 1e3 / (reps * per_graph)
+        tflops = 2.0 * m4 * n4 * k4 / (us4 * 1e-6) / 1e12
+        result["gemm_m1536_k3072_n3072"] = {
+            "tflops": round(tflops, 2), "us_per_call": round(us4, 3),
+            "peak_tflops": F16_MFMA_PEAK_TFLOPS, "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
+            "path": tq2.gemm_path(m4, n4, k4), "calls": reps * per_graph}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,145 @@
+// C ABI of libtq2: argument checks, device check, kernel selection.
+//
+// Error policy after the pages (oxibonsai-image 0.2.2, src/gpu.rs: the
+// `GpuMatmulError` enum and the doc of `ternary_matmul_gpu`): every failure,
+// including k % 128 != 0 and size mismatches, is returned to the caller and
+// nothing panics.  Unlike the pages there is no CPU fallback behind it.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/tq2.h"
+#include "tq2_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_device_kind[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TQ2_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int kind = g_device_kind[dev].load(std::memory_order_relaxed);
+    if (kind == 1) return TQ2_OK;
+    if (kind == 2) return TQ2_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TQ2_ERR_DEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_device_kind[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? TQ2_OK : TQ2_ERR_DEVICE;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;   // keeps every 32-bit index in range
+
+// Shape check shared by every entry point; m may be 0 (no-op) where allowed.
+int check_shape(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k <= 0) return TQ2_ERR_INVALID;
+  if (k % tq2::kBlockWeights) return TQ2_ERR_SHAPE;
+  if (m > kMaxDim || n > kMaxDim || k > kMaxDim) return TQ2_ERR_INVALID;
+  return TQ2_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? TQ2_OK : TQ2_ERR_LAUNCH; }
+
+// Checks common to tq2_gemv and tq2_gemm once the shape is valid and non-empty.
+int check_matmul_args(const void* soa, const float* x, const float* residual, const float* out,
+                      int64_t m, int64_t n, int64_t k) {
+  if (!soa || !x || !out) return TQ2_ERR_INVALID;
+  if (!aligned(soa, 256) || !aligned(x, 16) || !aligned(out, 16) ||
+      (residual && !aligned(residual, 16)))
+    return TQ2_ERR_ALIGN;
+  const size_t xb = size_t(m) * size_t(k) * 4, ob = size_t(m) * size_t(n) * 4;
+  const size_t sb = tq2::soa_bytes(n, k);
+  if (overlaps(out, ob, x, xb) || overlaps(out, ob, soa, sb)) return TQ2_ERR_ALIAS;
+  if (residual && residual != out && overlaps(out, ob, residual, ob)) return TQ2_ERR_ALIAS;
+  return check_device();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq2_aos_bytes(int64_t n, int64_t k) {
+  if (check_shape(0, n, k) != TQ2_OK) return 0;
+  return size_t(n) * size_t(k / tq2::kBlockWeights) * tq2::kBlockBytes;
+}
+
+size_t tq2_soa_bytes(int64_t n, int64_t k) {
+  if (check_shape(0, n, k) != TQ2_OK) return 0;
+  return tq2::soa_bytes(n, k);
+}
+
+int tq2_soa_layout_version(void) { return tq2::kLayoutVersion; }
+
+int tq2_reformat_aos_to_soa(const void* aos, void* soa, int64_t n, int64_t k, void* stream) {
+  int st = check_shape(0, n, k);
+  if (st != TQ2_OK) return st;
+  if (n == 0) return TQ2_OK;
+  if (!aos || !soa) return TQ2_ERR_INVALID;
+  if (!aligned(aos, 2) || !aligned(soa, 256)) return TQ2_ERR_ALIGN;
+  if (overlaps(aos, tq2_aos_bytes(n, k), soa, tq2::soa_bytes(n, k))) return TQ2_ERR_ALIAS;
+  st = check_device();
+  if (st != TQ2_OK) return st;
+  return launch_status(tq2::launch_reformat(static_cast<const uint16_t*>(aos),
+                                            static_cast<uint8_t*>(soa), n, k,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int tq2_gemm_path(int64_t m, int64_t n, int64_t k) {
+  const int st = check_shape(m, n, k);
+  if (st != TQ2_OK) return st;
+  if (m <= 1) return 0;
+  return m <= tq2::kSplitMaxM ? 1 : 2;
+}
+
+int tq2_gemv(const void* soa, const float* x, const float* residual, float* out, int64_t n,
+             int64_t k, void* stream) {
+  int st = check_shape(1, n, k);
+  if (st != TQ2_OK) return st;
+  if (n == 0) return TQ2_OK;
+  st = check_matmul_args(soa, x, residual, out, 1, n, k);
+  if (st != TQ2_OK) return st;
+  return launch_status(tq2::launch_gemv(static_cast<const uint8_t*>(soa), x, residual, out, n,
+                                        k, static_cast<hipStream_t>(stream)));
+}
+
+int tq2_gemm(const void* soa, const float* x, const float* residual, float* out, int64_t m,
+             int64_t n, int64_t k, void* stream) {
+  int st = check_shape(m, n, k);
+  if (st != TQ2_OK) return st;
+  if (m == 0 || n == 0) return TQ2_OK;
+  st = check_matmul_args(soa, x, residual, out, m, n, k);
+  if (st != TQ2_OK) return st;
+  const int path = tq2_gemm_path(m, n, k);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (path == 0)
+    return launch_status(
+        tq2::launch_gemv(static_cast<const uint8_t*>(soa), x, residual, out, n, k, s));
+  return launch_status(
+      tq2::launch_gemm(path, static_cast<const uint8_t*>(soa), x, residual, out, m, n, k, s));
+}
+
+const char* tq2_status_string(int status) {
+  switch (status) {
+    case TQ2_OK: return "ok";
+    case TQ2_ERR_INVALID: return "invalid argument (null pointer, negative or oversized dimension, k <= 0)";
+    case TQ2_ERR_SHAPE: return "k is not a multiple of 128";
+    case TQ2_ERR_ALIGN: return "misaligned pointer (soa needs 256 bytes, x/out/residual 16 bytes)";
+    case TQ2_ERR_ALIAS: return "output overlaps an input (only out == residual is allowed)";
+    case TQ2_ERR_DEVICE: return "current HIP device is not gfx950 or cannot be queried";
+    case TQ2_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown tq2 status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal declarations shared by the libtq2 translation units (not installed).
+//
+// Private SoA layout, version 1, of an [N, K] weight (KB = K / 128 blocks per
+// row), written by tq2_reformat_aos_to_soa:
+//
+//   codes plane  at byte 0:            N * K/4 bytes, row n at n * K/4.
+//                Row n is K/16 little-endian 32-bit words; word w holds the
+//                codes of k = 16w .. 16w+15.  Code of k = 16w + t sits at bit
+//                2*(t >> 1) + 16*(t & 1): even t in the low half-word, odd t
+//                in the high half-word, each half in increasing t.  Codes are
+//                stored canonical: 0 (-1), 1 (0), 2 (+1); a reserved code 3 is
+//                stored as 1.
+//   scales plane at byte align256(N*K/4):  binary16 d[n * KB + kb].
+//   total size  align256(scales offset + N*KB*2).
+//
+// The half-word split lets one AND-OR with 0x64006400 place the codes of two
+// neighbouring weights (k, k+1) into the mantissas of a binary16 pair, which
+// is the operand order of both the dot2 and the MFMA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq2 {
+
+constexpr int kBlockWeights = 128;
+constexpr int kBlockBytes = 34;
+constexpr int kLayoutVersion = 1;
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+inline size_t codes_bytes(int64_t n, int64_t k) { return size_t(n) * size_t(k / 4); }
+inline size_t scales_offset(int64_t n, int64_t k) { return align256(codes_bytes(n, k)); }
+inline size_t soa_bytes(int64_t n, int64_t k) {
+  return align256(scales_offset(n, k) + size_t(n) * size_t(k / kBlockWeights) * 2);
+}
+
+// Kernel launchers (one per translation unit).  Arguments are already
+// validated by the C ABI; each returns the hipError_t of its launch.
+hipError_t launch_reformat(const uint16_t* aos, uint8_t* soa, int64_t n, int64_t k,
+                           hipStream_t stream);
+hipError_t launch_gemv(const uint8_t* soa, const float* x, const float* residual, float* out,
+                       int64_t n, int64_t k, hipStream_t stream);
+hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float* residual,
+                       float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
+// Largest M served by the split-f16 (f32-class) matrix-core path.
+constexpr int64_t kSplitMaxM = 16;
+
+}  // namespace tq2

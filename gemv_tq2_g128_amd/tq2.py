@@ -1,0 +1,223 @@
+"""Python binding of libtq2, the gfx950 TQ2_0_g128 ternary matmul.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libtq2.so``; PyTorch provides device memory and streams.  There
+is no CPU fallback: importing this package fails loudly when the library has
+not been built (``python -m gemv_tq2_g128_amd.build``).
+
+The C entry points are declared in ``include/tq2.h``; the functions here have
+the same names without the ``tq2_`` prefix.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libtq2.so")
+
+TQ2_OK = 0
+TQ2_ERR_INVALID = -1
+TQ2_ERR_SHAPE = -2
+TQ2_ERR_ALIGN = -3
+TQ2_ERR_ALIAS = -4
+TQ2_ERR_DEVICE = -5
+TQ2_ERR_LAUNCH = -6
+
+PATH_GEMV = 0
+PATH_SPLIT_F16 = 1
+PATH_F16 = 2
+
+EXPORTED_SYMBOLS = (
+    "tq2_aos_bytes",
+    "tq2_soa_bytes",
+    "tq2_soa_layout_version",
+    "tq2_reformat_aos_to_soa",
+    "tq2_gemv",
+    "tq2_gemm",
+    "tq2_gemm_path",
+    "tq2_status_string",
+)
+
+
+def _hip_runtimes_mapped():
+    """Distinct HIP runtime files mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libtq2.so is not built (expected at %s); run "
+            "`python -m gemv_tq2_g128_amd.build`" % LIB_PATH)
+    # PyTorch ships its own HIP runtime.  Loading torch first makes libtq2's
+    # dependency on libamdhip64.so.7 resolve to that same runtime (same
+    # soname), so device pointers and streams from torch are valid in libtq2.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded (%s); import torch before loading "
+                          "libtq2 by any other route" % ", ".join(runtimes))
+    i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    c_int = ctypes.c_int
+    lib.tq2_aos_bytes.argtypes = [i64, i64]
+    lib.tq2_aos_bytes.restype = sz
+    lib.tq2_soa_bytes.argtypes = [i64, i64]
+    lib.tq2_soa_bytes.restype = sz
+    lib.tq2_soa_layout_version.argtypes = []
+    lib.tq2_soa_layout_version.restype = c_int
+    lib.tq2_reformat_aos_to_soa.argtypes = [vp, vp, i64, i64, vp]
+    lib.tq2_reformat_aos_to_soa.restype = c_int
+    lib.tq2_gemv.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    lib.tq2_gemv.restype = c_int
+    lib.tq2_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.tq2_gemm.restype = c_int
+    lib.tq2_gemm_path.argtypes = [i64, i64, i64]
+    lib.tq2_gemm_path.restype = c_int
+    lib.tq2_status_string.argtypes = [c_int]
+    lib.tq2_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+class TQ2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_string(status), status))
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ2_OK:
+        raise TQ2Error(status, where)
+
+
+# ---------------------------------------------------------------------------
+# Host-only queries.
+# ---------------------------------------------------------------------------
+
+def aos_bytes(n: int, k: int) -> int:
+    return int(lib.tq2_aos_bytes(n, k))
+
+
+def soa_bytes(n: int, k: int) -> int:
+    return int(lib.tq2_soa_bytes(n, k))
+
+
+def soa_layout_version() -> int:
+    return int(lib.tq2_soa_layout_version())
+
+
+def gemm_path(m: int, n: int, k: int) -> int:
+    return int(lib.tq2_gemm_path(m, n, k))
+
+
+def status_string(status: int) -> str:
+    return lib.tq2_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# Raw-pointer calls (device pointers and a hipStream_t as integers).
+# ---------------------------------------------------------------------------
+
+def reformat_aos_to_soa_ptr(aos_ptr: int, soa_ptr: int, n: int, k: int, stream: int = 0) -> int:
+    return int(lib.tq2_reformat_aos_to_soa(aos_ptr, soa_ptr, n, k, stream or None))
+
+
+def gemv_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, n: int, k: int,
+             stream: int = 0) -> int:
+    return int(lib.tq2_gemv(soa_ptr, x_ptr, residual_ptr or None, out_ptr, n, k, stream or None))
+
+
+def gemm_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, n: int, k: int,
+             stream: int = 0) -> int:
+    return int(lib.tq2_gemm(soa_ptr, x_ptr, residual_ptr or None, out_ptr, m, n, k,
+                            stream or None))
+
+
+# ---------------------------------------------------------------------------
+# torch.Tensor front end.
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t, dtype, numel: int, what: str):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % what)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % what)
+    if t.dtype != dtype:
+        raise ValueError("%s must have dtype %s, got %s" % (what, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    if t.numel() != numel:
+        raise ValueError("%s must have %d elements, got %d" % (what, numel, t.numel()))
+
+
+def reformat_aos_to_soa(aos, n: int, k: int, out=None):
+    """AoS block bytes (uint8 device tensor) -> resident SoA weight (uint8)."""
+    torch = _torch()
+    nbytes = aos_bytes(n, k)
+    if nbytes == 0 and n != 0:
+        _check(TQ2_ERR_SHAPE if k > 0 else TQ2_ERR_INVALID, "reformat_aos_to_soa")
+    _require(aos, torch.uint8, nbytes, "aos")
+    if out is None:
+        out = torch.empty(soa_bytes(n, k), dtype=torch.uint8, device=aos.device)
+    _require(out, torch.uint8, soa_bytes(n, k), "soa")
+    _check(reformat_aos_to_soa_ptr(aos.data_ptr(), out.data_ptr(), n, k,
+                                   _stream_handle(aos.device)), "reformat_aos_to_soa")
+    return out
+
+
+def gemv(soa, x, n: int, k: int, residual=None, out=None):
+    """out[n] = residual[n] + sum_k x[k] * w[n, k]; x is f32 [k] (or [1, k])."""
+    torch = _torch()
+    _require(soa, torch.uint8, soa_bytes(n, k), "soa")
+    _require(x, torch.float32, k, "x")
+    if residual is not None:
+        _require(residual, torch.float32, n, "residual")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=x.device)
+    _require(out, torch.float32, n, "out")
+    _check(gemv_ptr(soa.data_ptr(), x.data_ptr(),
+                    residual.data_ptr() if residual is not None else 0,
+                    out.data_ptr(), n, k, _stream_handle(x.device)), "gemv")
+    return out
+
+
+def gemm(soa, x, n: int, k: int, residual=None, out=None):
+    """out[m, n] = residual[m, n] + sum_k x[m, k] * w[n, k]; x is f32 [m, k]."""
+    torch = _torch()
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m, %d]" % k)
+    m = x.shape[0]
+    _require(soa, torch.uint8, soa_bytes(n, k), "soa")
+    _require(x, torch.float32, m * k, "x")
+    if residual is not None:
+        _require(residual, torch.float32, m * n, "residual")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _require(out, torch.float32, m * n, "out")
+    _check(gemm_ptr(soa.data_ptr(), x.data_ptr(),
+                    residual.data_ptr() if residual is not None else 0,
+                    out.data_ptr(), m, n, k, _stream_handle(x.device)), "gemm")
+    return out

@@ -1,0 +1,119 @@
+/*
+ * tq2.h -- C ABI of libtq2, the MI355X (gfx950) TQ2_0_g128 ternary matmul.
+ *
+ * The operation (oxibonsai-image 0.2.2, src/gpu.rs: module doc "Correctness
+ * contract" and the doc of `ternary_matmul_gpu`):
+ *
+ *     out[m, n] = residual[m, n] + sum_k x[m, k] * dequant(W)[n, k]
+ *
+ * with x row-major f32 [M, K], W out-major [N, K] (no transpose) and out
+ * row-major f32 [M, N].  The residual term is optional; it mirrors the fused
+ * `*_residual` kernels of oxibonsai-kernels 0.1.5 (pipelines.rs,
+ * `MetalPipelines` fields `gemv_q1_g128_v7_residual`,
+ * `gemm_q1_g128_v7_residual`) and is added once to the finished dot product.
+ *
+ * Weight format (gpu.rs, doc of `blocks_as_bytes`): N * (K / 128) blocks of
+ * 34 bytes, `qs[32]` then a little-endian binary16 scale `d`; row n's blocks
+ * are contiguous, block index increasing with k.  Recorded convention (the
+ * pages give neither): weight j of a block has code
+ * (qs[j / 4] >> (2 * (j % 4))) & 3, and codes 0, 1, 2 mean -1, 0, +1 times d;
+ * code 3 is reserved and means 0.
+ *
+ * Like the pages' kernel, the library runs on a resident re-laid-out copy of
+ * the weight (gpu.rs: `blocks_as_bytes` feeds `reformat_tq2_aos_to_soa`, and
+ * `ternary_matmul_gpu` keeps the resulting buffer resident): callers convert
+ * each weight once with tq2_reformat_aos_to_soa and pass the result to
+ * tq2_gemv / tq2_gemm.  That "SoA" layout is private to the library and
+ * versioned by tq2_soa_layout_version(); only its size is public.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers on the current HIP device, owned by the
+ *     caller.  The library never allocates, frees or keeps them.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call only enqueues work on it and returns; nothing synchronises.  The
+ *     returned status covers argument checks and the launch; faults during
+ *     execution surface at the caller's next synchronisation.
+ *   - Errors are returned as negative tq2_status values; nothing aborts.
+ *     Nothing is enqueued when a call returns an error.
+ *   - Calls are stateless and thread-safe; calls on different streams may run
+ *     concurrently.
+ */
+#ifndef TQ2_H
+#define TQ2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq2_status {
+  TQ2_OK = 0,
+  TQ2_ERR_INVALID = -1, /* null pointer, negative size, K <= 0, size too large */
+  TQ2_ERR_SHAPE = -2,   /* K is not a multiple of 128 (gpu.rs: `ternary_matmul_gpu` errors) */
+  TQ2_ERR_ALIGN = -3,   /* soa not 256-byte aligned, or x / out / residual not 16-byte aligned */
+  TQ2_ERR_ALIAS = -4,   /* out overlaps x or soa, residual partially overlaps out, aos overlaps soa */
+  TQ2_ERR_DEVICE = -5,  /* current HIP device is not gfx950, or HIP could not be queried */
+  TQ2_ERR_LAUNCH = -6   /* the kernel launch failed */
+} tq2_status;
+
+/* Bytes of an [n, k] weight in the 34-byte AoS block format: n * (k/128) * 34.
+ * Returns 0 for n < 0, k <= 0 or k % 128 != 0. */
+size_t tq2_aos_bytes(int64_t n, int64_t k);
+
+/* Bytes the library's resident SoA copy of an [n, k] weight occupies
+ * (a multiple of 256).  Returns 0 for invalid n, k as above. */
+size_t tq2_soa_bytes(int64_t n, int64_t k);
+
+/* Version number of the private SoA layout written by tq2_reformat_aos_to_soa. */
+int tq2_soa_layout_version(void);
+
+/* Convert an [n, k] weight from AoS blocks (`aos`, tq2_aos_bytes(n, k) bytes,
+ * any alignment of 2 bytes or more) to the library's SoA layout (`soa`,
+ * tq2_soa_bytes(n, k) bytes, 256-byte aligned).  The AoS->SoA step the pages
+ * name `reformat_tq2_aos_to_soa` (gpu.rs, doc of `blocks_as_bytes`); this
+ * library's layout is its own.  `aos` and `soa` must not overlap.
+ * n == 0 is a no-op.  Errors: INVALID, SHAPE, ALIGN (aos odd or soa not
+ * 256-aligned), ALIAS, DEVICE, LAUNCH. */
+int tq2_reformat_aos_to_soa(const void* aos, void* soa, int64_t n, int64_t k, void* stream);
+
+/* Decode GEMV (M = 1): out[n] = residual[n] + sum_k x[k] * w[n, k].
+ * soa: tq2_soa_bytes(n, k) bytes from tq2_reformat_aos_to_soa.  x: f32 [k].
+ * residual: f32 [n] or NULL.  out: f32 [n]; may be the same pointer as
+ * residual (in-place add), must not overlap x or soa otherwise.
+ * Arithmetic: f32 products and sums in short chains; error within
+ * 1e-5 * (sum_k |x[k] w[n,k]| + |residual[n]|).  Kernel of the pages' decode
+ * path: oxibonsai-kernels 0.1.5, pipelines.rs, field `gemv_tq2_g128_v1`.
+ * n == 0 is a no-op.  Errors: INVALID, SHAPE, ALIGN, ALIAS, DEVICE, LAUNCH. */
+int tq2_gemv(const void* soa, const float* x, const float* residual, float* out,
+             int64_t n, int64_t k, void* stream);
+
+/* Batched matmul for any M >= 1: out[m, n] = residual[m, n] + sum_k x[m, k] w[n, k].
+ * x: f32 [m, k] row-major; residual: f32 [m, n] or NULL; out: f32 [m, n],
+ * same aliasing rules as tq2_gemv.  The kernel is picked by tq2_gemm_path:
+ *   0: M == 1, the GEMV above;
+ *   1: 2 <= M <= 16: matrix-core GEMM with x split into two binary16 parts
+ *      (x = hi + lo), error within 1e-5 * sum|x w| for |x| <= 65504;
+ *   2: M > 16: matrix-core GEMM with x rounded to binary16 and weights staged
+ *      as exact binary16 code * d (oxibonsai-kernels 0.1.5, pipelines.rs,
+ *      fields `gemm_tq2_g128_v9_simdgroup` / `gemm_tq2_g128_v10_simdgroup`:
+ *      f16-staged operands, f32 accumulation); error within
+ *      2e-3 * sum|x w| for |x| <= 65504.
+ * m == 0 or n == 0 is a no-op.  Errors: INVALID, SHAPE, ALIGN, ALIAS, DEVICE,
+ * LAUNCH. */
+int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
+             int64_t m, int64_t n, int64_t k, void* stream);
+
+/* The kernel tq2_gemm uses for this shape (0, 1 or 2 as listed above), or
+ * TQ2_ERR_INVALID / TQ2_ERR_SHAPE for an invalid shape.  Pure host function. */
+int tq2_gemm_path(int64_t m, int64_t n, int64_t k);
+
+/* Static description of a status value ("ok", "invalid argument", ...). */
+const char* tq2_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ2_H */

@@ -1,0 +1,108 @@
+"""CPU checks of libtq2: it loads, exports every symbol of include/tq2.h, and
+its host-side logic (sizes, path choice, argument checks) behaves as the
+header says.  No kernel is launched: every call below either is a pure host
+function or is rejected before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from gemv_tq2_g128_amd import tq2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "tq2.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) == 8
+    assert sorted(tq2.EXPORTED_SYMBOLS) == names
+    lib = ctypes.CDLL(tq2.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_sizes():
+    assert tq2.aos_bytes(1, 128) == 34
+    assert tq2.aos_bytes(2, 128) == 68 == tq2.aos_bytes(1, 256)
+    assert tq2.aos_bytes(4096, 4096) == 4456448
+    assert tq2.aos_bytes(11008, 4096) == 11976704
+    assert tq2.aos_bytes(3072, 3072) == 2506752
+    for bad in [(1, 100), (1, 0), (-1, 128), (1, -128)]:
+        assert tq2.aos_bytes(*bad) == 0 and tq2.soa_bytes(*bad) == 0
+    for n, k in [(1, 128), (3, 384), (4096, 4096), (11008, 4096), (77, 12288)]:
+        s = tq2.soa_bytes(n, k)
+        assert s % 256 == 0
+        assert s >= n * k // 4 + n * (k // 128) * 2
+        assert s < n * k // 4 + n * (k // 128) * 2 + 512
+    assert tq2.soa_layout_version() == 1
+
+
+def test_gemm_path():
+    assert tq2.gemm_path(1, 4096, 4096) == tq2.PATH_GEMV
+    for m in (2, 7, 8, 9, 16):
+        assert tq2.gemm_path(m, 11008, 4096) == tq2.PATH_SPLIT_F16
+    for m in (17, 100, 1536):
+        assert tq2.gemm_path(m, 3072, 3072) == tq2.PATH_F16
+    assert tq2.gemm_path(8, 10, 100) == tq2.TQ2_ERR_SHAPE
+    assert tq2.gemm_path(8, 10, 0) == tq2.TQ2_ERR_INVALID
+    assert tq2.gemm_path(-1, 10, 128) == tq2.TQ2_ERR_INVALID
+    assert tq2.gemm_path(8, 10, 1 << 31) == tq2.TQ2_ERR_INVALID
+
+
+def test_status_strings():
+    for st in range(0, -7, -1):
+        s = tq2.status_string(st)
+        assert s and s != "unknown tq2 status"
+    assert tq2.status_string(-99) == "unknown tq2 status"
+
+
+# Fake, never-dereferenced addresses: every call below fails its host-side
+# checks before the library touches the device.
+A = 0x7F0000000000          # 256-byte aligned
+
+
+def test_argument_checks_before_any_device_work():
+    g, v, r = tq2.gemm_ptr, tq2.gemv_ptr, tq2.reformat_aos_to_soa_ptr
+    assert g(A, A + 0x100000, 0, A + 0x200000, 4, 8, 100) == tq2.TQ2_ERR_SHAPE
+    assert g(A, A + 0x100000, 0, A + 0x200000, 4, 8, 0) == tq2.TQ2_ERR_INVALID
+    assert g(A, A + 0x100000, 0, A + 0x200000, -4, 8, 128) == tq2.TQ2_ERR_INVALID
+    assert g(0, A + 0x100000, 0, A + 0x200000, 4, 8, 128) == tq2.TQ2_ERR_INVALID
+    assert g(A, 0, 0, A + 0x200000, 4, 8, 128) == tq2.TQ2_ERR_INVALID
+    assert g(A, A + 0x100000, 0, 0, 4, 8, 128) == tq2.TQ2_ERR_INVALID
+    assert g(A + 64, A + 0x100000, 0, A + 0x200000, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert g(A, A + 0x100004, 0, A + 0x200000, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert g(A, A + 0x100000, A + 0x300008, A + 0x200000, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    # out overlapping x, the weight, or part of the residual
+    assert g(A, A + 0x100000, 0, A + 0x100000 + 16, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert g(A, A + 0x100000, 0, A + 16 * 16, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert g(A, A + 0x100000, A + 0x200010, A + 0x200000, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert v(A, A + 0x100000, 0, A + 0x100000, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert v(A, A + 0x100000, 0, A + 0x200000, 8, 200) == tq2.TQ2_ERR_SHAPE
+    assert r(A + 1, A + 0x100000, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert r(A, A + 0x100010, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert r(A, A, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert r(0, A, 8, 128) == tq2.TQ2_ERR_INVALID
+    # empty shapes are no-ops that touch nothing, even with null pointers
+    assert g(0, 0, 0, 0, 0, 8, 128) == tq2.TQ2_OK
+    assert g(0, 0, 0, 0, 4, 0, 128) == tq2.TQ2_OK
+    assert v(0, 0, 0, 0, 0, 128) == tq2.TQ2_OK
+    assert r(0, 0, 0, 128) == tq2.TQ2_OK
+
+
+def test_device_check_without_gpu():
+    """Valid arguments but no gfx950 device: the call must return
+    TQ2_ERR_DEVICE (never crash).  Only meaningful where no GPU is visible."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; this check is for GPU-less hosts")
+    st = tq2.gemm_ptr(A, A + 0x100000, 0, A + 0x200000, 4, 8, 128)
+    assert st == tq2.TQ2_ERR_DEVICE

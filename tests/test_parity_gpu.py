@@ -1,0 +1,265 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every case draws seeded inputs from ``tq2_inputs``, runs the library on the
+GPU and compares element by element with ``oracle`` (float64) within the
+tolerance of the kernel path that ran (see tests/parity.py).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import tq2_inputs as G
+from tests.parity import check
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tq2():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    from gemv_tq2_g128_amd import tq2 as mod
+    return mod
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def upload_weight(tq2, aos, n, k):
+    return tq2.reformat_aos_to_soa(_dev(aos), n, k)
+
+
+def run_case(tq2, case, force_gemv=False, inplace=False):
+    m, n, k = case["m"], case["n"], case["k"]
+    soa = upload_weight(tq2, case["aos"], n, k)
+    x = _dev(case["x"].reshape(m, k))
+    res = _dev(case["residual"].reshape(m, n)) if case["residual"] is not None else None
+    out = res.clone() if (inplace and res is not None) else None
+    res_arg = out if inplace and res is not None else res
+    if force_gemv:
+        assert m == 1
+        y = tq2.gemv(soa, x.reshape(-1), n, k, residual=None if res_arg is None else res_arg.reshape(-1),
+                     out=None if out is None else out.reshape(-1))
+    else:
+        y = tq2.gemm(soa, x, n, k, residual=res_arg, out=out)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().reshape(m, n)
+
+
+def oracle_full(case):
+    ref = oracle.matmul(case["aos"], case["x"], case["n"], case["k"], case["residual"])
+    s = oracle.error_scale(case["aos"], case["x"], case["n"], case["k"], case["residual"])
+    return ref, s
+
+
+def assert_case(tq2, case, **kw):
+    print("case", case["name"], kw, flush=True)
+    got = run_case(tq2, case, **kw)
+    ref, s = oracle_full(case)
+    path = 0 if kw.get("force_gemv") else tq2.gemm_path(case["m"], case["n"], case["k"])
+    ok, msg = check(got, ref, s, path, case["name"])
+    print(msg, flush=True)
+    assert ok, msg
+    return got
+
+
+# ---------------------------------------------------------------------------
+# Reformat: byte-exact against the documented private layout (version 1).
+# ---------------------------------------------------------------------------
+
+def host_soa_v1(aos, n, k):
+    """SoA v1 built on the host from the layout description in tq2_internal.h:
+    codes plane [n][k/4] with the code of k = 16w + t of word w at bit
+    2*(t>>1) + 16*(t&1), code 3 stored as 1; binary16 scales [n][k/128] at
+    align256(n*k/4); total rounded up to 256."""
+    blk = aos.reshape(n * (k // 128), 34)
+    qs = blk[:, :32].reshape(-1)
+    bits = np.unpackbits(qs, bitorder="little").reshape(-1, 16, 2)   # [words, t, bit]
+    codes = bits[:, :, 0].astype(np.uint32) | (bits[:, :, 1].astype(np.uint32) << 1)
+    codes = np.where(codes == 3, 1, codes)
+    t = np.arange(16)
+    shift = (2 * (t >> 1) + 16 * (t & 1)).astype(np.uint32)
+    words = np.bitwise_or.reduce(codes << shift[None, :], axis=1).astype("<u4")
+    code_bytes = words.view(np.uint8)
+    off = (code_bytes.size + 255) // 256 * 256
+    total = (off + n * (k // 128) * 2 + 255) // 256 * 256
+    out = np.zeros(total, dtype=np.uint8)
+    out[: code_bytes.size] = code_bytes
+    out[off: off + n * (k // 128) * 2] = blk[:, 32:].reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("n,k,seed", [(1, 128, 1), (3, 384, 2), (17, 1024, 3), (64, 4096, 4)])
+def test_reformat_matches_layout(tq2, n, k, seed):
+    assert tq2.soa_layout_version() == 1
+    case = G.random_case(seed, 1, n, k, probs=(0.3, 0.3, 0.3, 0.1))   # includes code 3
+    soa = upload_weight(tq2, case["aos"], n, k)
+    torch.cuda.synchronize()
+    got = soa.cpu().numpy()
+    want = host_soa_v1(case["aos"], n, k)
+    assert got.size == want.size == tq2.soa_bytes(n, k)
+    off = (n * k // 4 + 255) // 256 * 256
+    used = np.zeros(got.size, bool)
+    used[: n * k // 4] = True
+    used[off: off + n * (k // 128) * 2] = True
+    assert np.array_equal(got[used], want[used])
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at their full sizes.
+# ---------------------------------------------------------------------------
+
+def test_config1_gemv(tq2):
+    c = G.config1()
+    assert_case(tq2, c, force_gemv=True)
+    assert_case(tq2, c)
+
+
+def test_config2_gemv(tq2):
+    assert_case(tq2, G.config2(False), force_gemv=True)
+
+
+def test_config2_gemv_residual(tq2):
+    c = G.config2(True)
+    assert_case(tq2, c, force_gemv=True)
+    assert_case(tq2, c, force_gemv=True, inplace=True)
+
+
+@pytest.mark.parametrize("m", [7, 8, 9, 100])
+def test_config3_gemm(tq2, m):
+    assert_case(tq2, G.config3(m))
+
+
+def test_config4_gemm(tq2):
+    assert_case(tq2, G.config4())
+
+
+def test_config5_chain_sampled(tq2):
+    """100 chained layers at M=1536; every layer checked (teacher forced: the
+    oracle consumes the GPU's actual layer input) on 48 sampled columns."""
+    x = _dev(G.chain_input())
+    rng = np.random.default_rng(55)
+    for layer in range(G.CHAIN_LAYERS):
+        k, n = G.chain_layer_shape(layer)
+        aos = G.chain_layer_weight(layer)
+        soa = upload_weight(tq2, aos, n, k)
+        y = tq2.gemm(soa, x, n, k)
+        torch.cuda.synchronize()
+        cols = rng.choice(n, size=48, replace=False)
+        ref, s = oracle.matmul_rows(aos, x.cpu().numpy(), n, k, cols)
+        got = y[:, torch.from_numpy(cols).cuda()].cpu().numpy()
+        ok, msg = check(got, ref, s, tq2.gemm_path(G.CHAIN_M, n, k), "layer %d" % layer)
+        assert ok, msg
+        # next input: first 3072 columns, RMS-rescaled per row (harness glue)
+        nxt = y[:, : G.chain_layer_shape(layer + 1)[0]]
+        x = (nxt / torch.sqrt(torch.mean(nxt * nxt, dim=1, keepdim=True) + 1e-6)).contiguous()
+        del soa
+
+
+# ---------------------------------------------------------------------------
+# Shapes: several tiles plus ragged tails in M, N and K.
+# ---------------------------------------------------------------------------
+
+GEMV_SHAPES = [(1, 128), (5, 256), (63, 384), (64, 1024), (65, 2176), (300, 4096),
+               (129, 8192), (77, 12288), (33, 16384), (40, 20480)]
+
+
+@pytest.mark.parametrize("n,k", GEMV_SHAPES)
+def test_gemv_shapes(tq2, n, k):
+    c = G.random_case(1000 + n + k, 1, n, k, residual=True)
+    assert_case(tq2, c, force_gemv=True)
+
+
+GEMM_SHAPES = [(2, 17, 128), (3, 100, 384), (8, 64, 256), (15, 65, 640), (16, 257, 1024),
+               (17, 200, 384), (31, 33, 128), (32, 300, 512), (33, 100, 256), (64, 129, 384),
+               (65, 64, 1024), (96, 192, 256), (97, 250, 640), (128, 300, 512),
+               (129, 191, 384), (200, 385, 768), (300, 1000, 1152)]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+def test_gemm_shapes(tq2, m, n, k):
+    c = G.random_case(2000 + m + n + k, m, n, k, residual=True)
+    assert_case(tq2, c)
+    c2 = dict(c, residual=None, name=c["name"] + "_nores")
+    assert_case(tq2, c2)
+
+
+# ---------------------------------------------------------------------------
+# Edge values and degenerate cases.
+# ---------------------------------------------------------------------------
+
+def _blocks_with(case, qs_byte=None, d_bits=None):
+    a = case["aos"].reshape(-1, 34).copy()
+    if qs_byte is not None:
+        a[:, :32] = qs_byte
+    if d_bits is not None:
+        a[:, 32] = d_bits & 0xFF
+        a[:, 33] = d_bits >> 8
+    return dict(case, aos=a.reshape(-1))
+
+
+@pytest.mark.parametrize("m", [1, 4, 40])
+def test_special_codes_and_scales(tq2, m):
+    base = G.random_case(77 + m, m, 48, 512, residual=True)
+    for label, kw in [("code3", dict(qs_byte=0xFF)), ("all_zero_weight", dict(qs_byte=0x55)),
+                      ("all_plus", dict(qs_byte=0xAA)), ("all_minus", dict(qs_byte=0x00)),
+                      ("d_zero", dict(d_bits=0x0000)), ("d_negative", dict(d_bits=0xB400)),
+                      ("d_subnormal", dict(d_bits=0x0003)), ("d_max", dict(d_bits=0x7BFF))]:
+        c = dict(_blocks_with(base, **kw), name="%s_m%d" % (label, m))
+        assert_case(tq2, c)
+
+
+def test_zero_weight_gives_residual_exactly(tq2):
+    c = _blocks_with(G.random_case(5, 3, 40, 256, residual=True), qs_byte=0x55)
+    got = run_case(tq2, c)
+    assert np.array_equal(got, c["residual"].reshape(3, 40))
+    c1 = _blocks_with(G.random_case(6, 1, 40, 256, residual=True), qs_byte=0x55)
+    assert np.array_equal(run_case(tq2, c1, force_gemv=True), c1["residual"].reshape(1, 40))
+
+
+def test_large_activations_f16_range(tq2):
+    c = G.random_case(9, 64, 96, 256)
+    c["x"] = (c["x"] * np.float32(8000.0)).astype(np.float32)     # |x| up to ~4e4 < 65504
+    assert_case(tq2, c)
+
+
+def test_empty_shapes_are_noops(tq2):
+    soa = upload_weight(tq2, G.random_case(1, 1, 8, 128)["aos"], 8, 128)
+    x = torch.zeros((0, 128), device="cuda")
+    y = tq2.gemm(soa, x, 8, 128)
+    assert y.shape == (0, 8)
+    out = torch.full((4,), 7.0, device="cuda")
+    assert tq2.gemm_ptr(soa.data_ptr(), x.data_ptr(), 0, out.data_ptr(), 4, 0, 128) == 0
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_deterministic_and_stream_aware(tq2):
+    c = G.random_case(31, 37, 211, 640, residual=True)
+    a = run_case(tq2, c)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_case(tq2, c)
+    assert np.array_equal(a, b)
+
+
+def test_error_codes_with_device_pointers(tq2):
+    n, k, m = 32, 256, 4
+    soa = upload_weight(tq2, G.random_case(2, 1, n, k)["aos"], n, k)
+    x = torch.randn(m * k + 4, device="cuda")
+    out = torch.empty(m * n + 4, device="cuda")
+    res = torch.randn(m * n + 4, device="cuda")
+    p = tq2.gemm_ptr
+    assert p(soa.data_ptr(), x.data_ptr() + 4, 0, out.data_ptr(), m, n, k) == tq2.TQ2_ERR_ALIGN
+    assert p(soa.data_ptr() + 16, x.data_ptr(), 0, out.data_ptr(), m, n, k) == tq2.TQ2_ERR_ALIGN
+    assert p(soa.data_ptr(), x.data_ptr(), 0, x.data_ptr(), m, n, k) == tq2.TQ2_ERR_ALIAS
+    assert p(soa.data_ptr(), x.data_ptr(), res.data_ptr() + 16, res.data_ptr(), m, n, k) == \
+        tq2.TQ2_ERR_ALIAS
+    assert p(soa.data_ptr(), x.data_ptr(), 0, out.data_ptr(), m, n, 100) == tq2.TQ2_ERR_SHAPE
+    assert p(soa.data_ptr(), x.data_ptr(), 0, out.data_ptr(), -1, n, k) == tq2.TQ2_ERR_INVALID
+    assert p(0, x.data_ptr(), 0, out.data_ptr(), m, n, k) == tq2.TQ2_ERR_INVALID
+    assert p(soa.data_ptr(), x.data_ptr(), res.data_ptr(), res.data_ptr(), m, n, k) == tq2.TQ2_OK
+    torch.cuda.synchronize()

@@ -32,13 +32,29 @@ UNIFORM_TERNARY = (1.0 / 3.0, 1.0 / 3.0, 1.0 / 3.0, 0.0)
 HALF_ZERO_TERNARY = (0.25, 0.5, 0.25, 0.0)
 
 
+def _fields_to_byte(f0, f1, f2, f3):
+    return (f0 | (f1 << 2) | (f2 << 4) | (f3 << 6)).astype(np.uint8)
+
+
+# 81 base-3 digit patterns: a uniform integer in [0, 81) has four i.i.d. digits
+# uniform over {0, 1, 2}.
+_BASE3 = np.array([_fields_to_byte(np.uint8(v % 3), np.uint8(v // 3 % 3), np.uint8(v // 9 % 3),
+                                   np.uint8(v // 27 % 3)) for v in range(81)], dtype=np.uint8)
+# fields 0..3 -> codes 0, 1, 1, 2: probabilities 1/4, 1/2, 1/4
+_HALF_ZERO_FIELD = np.array([0, 1, 1, 2], dtype=np.uint8)
+
+
 def draw_code_bytes(rng: np.random.Generator, nbytes: int, probs) -> np.ndarray:
     """``nbytes`` bytes whose four 2-bit fields are i.i.d. with ``probs``."""
     p = np.asarray(probs, dtype=np.float64)
     p = p / p.sum()
-    fields = rng.choice(4, size=(nbytes, 4), p=p).astype(np.uint8)
-    return (fields[:, 0] | (fields[:, 1] << 2) | (fields[:, 2] << 4)
-            | (fields[:, 3] << 6)).astype(np.uint8)
+    if np.allclose(p, UNIFORM_TERNARY):
+        return _BASE3[rng.integers(0, 81, size=nbytes, dtype=np.uint8)]
+    if np.allclose(p, HALF_ZERO_TERNARY):
+        f = _HALF_ZERO_FIELD[rng.integers(0, 4, size=(4, nbytes), dtype=np.uint8)]
+        return _fields_to_byte(f[0], f[1], f[2], f[3])
+    f = rng.choice(4, size=(4, nbytes), p=p).astype(np.uint8)
+    return _fields_to_byte(f[0], f[1], f[2], f[3])
 
 
 def draw_scales_f16(rng: np.random.Generator, count: int, lo: float, hi: float) -> np.ndarray:
