@@ -121,6 +121,8 @@ int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
   st = check_matmul_args(soa, x, residual, out, m, n, k);
   if (st != TQ2_OK) return st;
   const int path = tq2_gemm_path(m, n, k);
+  if (path != 0 && (k > tq2::kGemmMaxK || n * (k / 4) >= tq2::kGemmMaxCodeBytes))
+    return TQ2_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (path == 0)
     return launch_status(

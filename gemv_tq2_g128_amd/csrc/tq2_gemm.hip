@@ -51,12 +51,24 @@ __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_c
 // `word` holds the step's codes in fields r = 0..3 at bits 2r (first weight
 // of pair r) and 2r + 16 (second weight).  (1024 + 4^r c) * 4^-r - (1024 *
 // 4^-r + 1) = c - 1 exactly; times d stays exact (+-d or 0).
-__device__ __forceinline__ half8_t decode_step(uint32_t word, half2_t d2) {
+// v_and_or_b32 with the mask in an SGPR and the constant in a VGPR (gfx9 VOP3
+// instructions take no literal operand).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
+}
+
+// Four binary16 pairs (8 weights) of one MFMA step from one code word.
+// `word` holds the step's codes in fields r = 0..3 at bits 2r (first weight
+// of pair r) and 2r + 16 (second weight).  (1024 + 4^r c) * 4^-r - (1024 *
+// 4^-r + 1) = c - 1 exactly; times d stays exact (+-d or 0).
+__device__ __forceinline__ half8_t decode_step(uint32_t word, half2_t d2, uint32_t magic) {
   half8_t b;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t mask = (3u << (2 * r)) | (3u << (2 * r + 16));
-    const half2_t v = as_half2((word & mask) | 0x64006400u);
+    const half2_t v = as_half2(and_or(word, mask, magic));
     const _Float16 sc = _Float16(1.0f / float(1 << (2 * r)));
     const _Float16 off = _Float16(-(1024.0f / float(1 << (2 * r)) + 1.0f));
     const half2_t scv = {sc, sc};
@@ -68,19 +80,37 @@ __device__ __forceinline__ half8_t decode_step(uint32_t word, half2_t d2) {
   return b;
 }
 
-template <int MT, int NW, int LIMBS>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint32_t* __restrict__ codes,
-                                                        const uint16_t* __restrict__ scales,
-                                                        const float* __restrict__ x,
-                                                        const float* __restrict__ residual,
-                                                        float* __restrict__ out, int M, int N,
-                                                        int K, int tiles_m, int tiles_n) {
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over `bytes` bytes at `base`: loads past the end
+// return zero, loads take a 32-bit per-lane offset plus a scalar offset.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
+                                           0x00020000);
+}
+
+// Block tile MT x (WN*NW); WN waves split the columns, WK waves split each
+// 256-wide chunk's eight MFMA steps (their partial sums meet in LDS at the
+// end).  Each wave owns MT rows x NW columns of the tile.
+template <int MT, int NW, int WN, int WK, int LIMBS>
+__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ x,
+                                                            const float* __restrict__ residual,
+                                                            float* __restrict__ out, int M, int N,
+                                                            int K, int tiles_m, int tiles_n) {
+  constexpr int THREADS = 64 * WN * WK;
   constexpr int RT = MT / 16;            // 16-row MFMA tiles per wave
   constexpr int CG = NW / 16;            // 16-column groups per wave
-  constexpr int NT = 4 * NW;
-  constexpr int AV = MT * (kChunk / 4) / kThreads;   // float4 A loads per thread per chunk
+  constexpr int NT = WN * NW;
+  constexpr int STEPS = 8 / WK;          // MFMA k-steps per wave per chunk
+  constexpr int QW = 4 / WK;             // code dwords per lane per chunk
+  constexpr int AV = MT * (kChunk / 4) / THREADS;   // float4 A loads per thread per chunk
   static_assert(MT % 16 == 0 && NW % 16 == 0, "tile shape");
-  static_assert((MT * (kChunk / 4)) % kThreads == 0, "A staging split");
+  static_assert(WK == 1 || WK == 2, "k split");
+  static_assert((MT * (kChunk / 4)) % THREADS == 0, "A staging split");
 
   __shared__ _Float16 As[2][LIMBS][MT][kLdsRow];
 
@@ -96,33 +126,43 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint32_t* __restri
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int wn = wave % WN;              // column share
+  const int wk = wave / WN;              // share of the chunk's steps
   const int lane = tid & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
   const int KB = K >> 7;
-  const int words_per_row = K >> 4;
   const int nchunks = (K + kChunk - 1) / kChunk;
 
-  // ---- staging helpers -------------------------------------------------
-  float4 areg[AV];
-  auto load_a = [&](int c) {
+  // x rows m0 .. m0+MT-1 (rows past M read as zero).
+  const rsrc_t rx = make_rsrc(x + size_t(m0) * K, uint32_t(min(MT, M - m0)) * uint32_t(K) * 4u);
+  const rsrc_t rc = make_rsrc(codes, uint32_t(N) * uint32_t(K / 4));
+  const rsrc_t rs = make_rsrc(scales, uint32_t(N) * uint32_t(KB) * 2u);
+
+  // Per-thread byte offsets, fixed for the whole K loop; a chunk, an A row
+  // step and a column group add scalar offsets.  Columns past N read as zero
+  // codes and zero scales.
+  const uint32_t aoff = uint32_t(tid >> 6) * uint32_t(K) * 4u + 16u * uint32_t(tid & 63);
+  constexpr int AROWS = THREADS / 64;    // A rows staged per load instruction
+  const uint32_t nl = uint32_t(n0 + wn * NW + col);
+  const uint32_t coff = nl * uint32_t(K / 4) + 16u * g + 4u * QW * wk;
+  const uint32_t soff = (nl * uint32_t(KB) + uint32_t(g >> 1)) * 2u;
+  const int cstep = 16 * (K / 4);        // bytes between 16-column groups
+  const int sstep = 16 * KB * 2;
+
+  typedef uint32_t codes_t[QW];
+  auto load_a = [&](int c, float4 (&areg)[AV]) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-      const int f = tid + kThreads * i;
-      const int r = f >> 6;              // kChunk / 4 = 64 float4 per row
-      const int c4 = f & 63;
-      const int m = m0 + r;
-      const int kk = c * kChunk + 4 * c4;
-      if (m < M && kk < K)
-        areg[i] = *reinterpret_cast<const float4*>(x + size_t(m) * K + kk);
-      else
-        areg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, aoff, i * AROWS * K * 4 + c * kChunk * 4, 0);
+      areg[i] = __builtin_bit_cast(float4, v);
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int buf, const float4 (&areg)[AV]) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
-      const int f = tid + kThreads * i;
+      const int f = tid + THREADS * i;
       const int r = f >> 6;
       const int c4 = f & 63;
       const float4 v = areg[i];
@@ -135,23 +175,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint32_t* __restri
       }
     }
   };
-
-  uint4 cw[CG];
-  uint32_t dw[CG];
-  auto load_w = [&](int c, uint4 (&cwo)[CG], uint32_t (&dwo)[CG]) {
+  auto load_w = [&](int c, codes_t (&cwo)[CG], uint32_t (&dwo)[CG]) {
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const int n = n0 + wave * NW + j * 16 + col;
-      const int kk = c * kChunk + 64 * g;
-      if (n < N && kk < K) {
-        cwo[j] = *reinterpret_cast<const uint4*>(codes + size_t(n) * words_per_row +
-                                                 (c * kChunk + 64 * g) / 16);
-        const uint32_t d = scales[size_t(n) * KB + 2 * c + (g >> 1)];
-        dwo[j] = d | (d << 16);
+      if constexpr (QW == 4) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, coff, j * cstep + c * 64, 0);
+        cwo[j][0] = v[0]; cwo[j][1] = v[1]; cwo[j][2] = v[2]; cwo[j][3] = v[3];
       } else {
-        cwo[j] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-        dwo[j] = 0u;
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, coff, j * cstep + c * 64, 0);
+        cwo[j][0] = v[0]; cwo[j][1] = v[1];
       }
+      dwo[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, j * sstep + c * 4, 0);
     }
   };
 
@@ -161,54 +195,132 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint32_t* __restri
 #pragma unroll
     for (int j = 0; j < CG; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue ---------------------------------------------------------
-  load_a(0);
-  load_w(0, cw, dw);
-  store_a(0);
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    const int buf = c & 1;
-    uint4 cwn[CG];
-    uint32_t dwn[CG];
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      load_a(c + 1);
-      load_w(c + 1, cwn, dwn);
+  const uint32_t magic = 0x64006400u;     // binary16 pair (1024, 1024)
+  // Operands of one MFMA step: A fragments from LDS, B fragments decoded
+  // from the code words.
+  auto load_afrags = [&](int buf, int s, half8_t (&a)[RT][LIMBS]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int l = 0; l < LIMBS; ++l)
+        a[i][l] = *reinterpret_cast<const half8_t*>(&As[buf][l][i * 16 + col][64 * g + 8 * s]);
+  };
+  auto decode_bfrags = [&](int ss, const codes_t (&cw)[CG], const uint32_t (&dw)[CG],
+                           half8_t (&b)[CG]) {
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      uint32_t w = cw[j][ss >> 1];
+      if (ss & 1) w >>= 8;
+      b[j] = decode_step(w, as_half2(dw[j]), magic);
     }
+  };
+  auto mfmas = [&](const half8_t (&a)[RT][LIMBS], const half8_t (&b)[CG]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int l = 0; l < LIMBS; ++l)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i][l], b[j], acc[i][j], 0, 0, 0);
+  };
+  // Ask the scheduler to interleave one step's MFMAs with the next step's
+  // operand work: per MFMA about VALU/MFMA decode instructions and an LDS
+  // read every few MFMAs, instead of long runs of either.
+  constexpr int NMFMA = RT * LIMBS * CG;
+  constexpr int NDSR = RT * LIMBS;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < NMFMA; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+      if (q % ((NMFMA + NDSR - 1) / NDSR) == 0)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);          // up to three VALU
+    }
+  };
 
+  auto compute = [&](int c, int buf, const codes_t (&cw)[CG], const uint32_t (&draw)[CG]) {
+    // binary16 pair (d, d), or (0, 0) where k runs past K in the last chunk.
+    const bool live = c * kChunk + 64 * g < K;
+    uint32_t dw[CG];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8_t bop[CG];
+    for (int j = 0; j < CG; ++j) dw[j] = live ? (draw[j] | (draw[j] << 16)) : 0u;
+    half8_t a0[RT][LIMBS], a1[RT][LIMBS], b0[CG], b1[CG];
+    load_afrags(buf, wk * STEPS, a0);
+    decode_bfrags(0, cw, dw, b0);
 #pragma unroll
-      for (int j = 0; j < CG; ++j) {
-        const uint32_t words[4] = {cw[j].x, cw[j].y, cw[j].z, cw[j].w};
-        uint32_t w = words[s >> 1];
-        if (s & 1) w >>= 8;
-        bop[j] = decode_step(w, as_half2(dw[j]));
-      }
-#pragma unroll
-      for (int i = 0; i < RT; ++i) {
-#pragma unroll
-        for (int l = 0; l < LIMBS; ++l) {
-          const half8_t aop =
-              *reinterpret_cast<const half8_t*>(&As[buf][l][i * 16 + col][64 * g + 8 * s]);
-#pragma unroll
-          for (int j = 0; j < CG; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[j], acc[i][j], 0, 0, 0);
+    for (int ss = 0; ss < STEPS; ++ss) {
+      const int s = wk * STEPS + ss;     // chunk step: k = 64g + 8s .. +7
+      if ((ss & 1) == 0) {
+        if (ss + 1 < STEPS) {
+          load_afrags(buf, s + 1, a1);
+          decode_bfrags(ss + 1, cw, dw, b1);
         }
+        mfmas(a0, b0);
+      } else {
+        if (ss + 1 < STEPS) {
+          load_afrags(buf, s + 1, a0);
+          decode_bfrags(ss + 1, cw, dw, b0);
+        }
+        mfmas(a1, b1);
       }
+      interleave();
+      // Keep the next step's operand loads inside this step's region so
+      // their latency hides behind this step's MFMAs.
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
+  // ---- software pipeline: loads run one chunk ahead of the MFMAs ---------
+  float4 areg[AV];
+  codes_t cw[CG];
+  uint32_t draw[CG];
+  load_a(0, areg);
+  load_w(0, cw, draw);
+  store_a(0, areg);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const bool more = c + 1 < nchunks;
+    codes_t cwn[CG];
+    uint32_t drawn[CG];
     if (more) {
-      store_a(buf ^ 1);
+      load_a(c + 1, areg);
+      load_w(c + 1, cwn, drawn);
+    }
+    compute(c, c & 1, cw, draw);
+    if (more) {
+      store_a((c & 1) ^ 1, areg);
 #pragma unroll
       for (int j = 0; j < CG; ++j) {
-        cw[j] = cwn[j];
-        dw[j] = dwn[j];
+#pragma unroll
+        for (int q = 0; q < QW; ++q) cw[j][q] = cwn[j][q];
+        draw[j] = drawn[j];
       }
     }
     __syncthreads();
+  }
+
+  // ---- K-split reduction: the wk = 1 waves hand their sums to wk = 0 -----
+  if constexpr (WK == 2) {
+    float* red = reinterpret_cast<float*>(&As[0][0][0][0]);
+    static_assert(WN * RT * CG * 4 * 64 * 4 <= sizeof(As), "reduction buffer");
+    if (wk == 1) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (wk == 1) return;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CG; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[i][j][e] += red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane];
   }
 
   // ---- epilogue: D[row = 4g + e][col] of each 16x16 tile -----------------
@@ -216,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint32_t* __restri
   for (int i = 0; i < RT; ++i) {
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const int n = n0 + wave * NW + j * 16 + col;
+      const int n = n0 + wn * NW + j * 16 + col;
       if (n >= N) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -232,17 +344,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint32_t* __restri
   }
 }
 
-template <int MT, int NW, int LIMBS>
-hipError_t launch_tile(const uint32_t* codes, const uint16_t* scales, const float* x,
-                       const float* residual, float* out, int64_t m, int64_t n, int64_t k,
-                       hipStream_t stream) {
+template <int MT, int NW, int WN, int WK, int LIMBS>
+hipError_t launch_tile(const uint8_t* soa, const float* x, const float* residual, float* out,
+                       int64_t m, int64_t n, int64_t k, hipStream_t stream) {
   const int64_t tm = (m + MT - 1) / MT;
-  const int64_t tn = (n + 4 * NW - 1) / (4 * NW);
+  const int64_t tn = (n + WN * NW - 1) / (WN * NW);
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = int(tm), tiles_n = int(tn);
   const dim3 grid(unsigned(tm * tn));
-  hipLaunchKernelGGL((gemm_kernel<MT, NW, LIMBS>), grid, dim3(kThreads), 0, stream, codes,
-                     scales, x, residual, out, int(m), int(n), int(k), tiles_m, tiles_n);
+  hipLaunchKernelGGL((gemm_kernel<MT, NW, WN, WK, LIMBS>), grid, dim3(64 * WN * WK), 0, stream,
+                     soa, soa + scales_offset(n, k), x, residual, out, int(m), int(n), int(k),
+                     tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -250,13 +362,11 @@ hipError_t launch_tile(const uint32_t* codes, const uint16_t* scales, const floa
 
 hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float* residual,
                        float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  const uint32_t* codes = reinterpret_cast<const uint32_t*>(soa);
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(soa + scales_offset(n, k));
-  if (path == 1) return launch_tile<16, 16, 2>(codes, scales, x, residual, out, m, n, k, stream);
-  if (m <= 32) return launch_tile<32, 16, 1>(codes, scales, x, residual, out, m, n, k, stream);
-  if (m <= 64) return launch_tile<64, 16, 1>(codes, scales, x, residual, out, m, n, k, stream);
-  if (m <= 128) return launch_tile<128, 16, 1>(codes, scales, x, residual, out, m, n, k, stream);
-  return launch_tile<96, 48, 1>(codes, scales, x, residual, out, m, n, k, stream);
+  if (path == 1) return launch_tile<16, 16, 4, 2, 2>(soa, x, residual, out, m, n, k, stream);
+  if (m <= 32) return launch_tile<32, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
+  if (m <= 64) return launch_tile<64, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
+  if (m <= 128) return launch_tile<128, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
+  return launch_tile<96, 48, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
 }
 
 }  // namespace tq2

@@ -3,148 +3,211 @@
 // The pages' decode kernel is `gemv_tq2_g128_v1` (oxibonsai-kernels 0.1.5,
 // pipelines.rs, `MetalPipelines`, ternary section); its source is not on the
 // pages.  The optional fused residual follows the `gemv_q1_g128_v7_residual`
-// entry of the same table.  This kernel is designed for gfx950 on its own:
+// entry of the same table.  This kernel is designed for gfx950 on its own.
 //
-//  * HBM stream: every lane reads 16 contiguous code bytes (64 weights) of a
-//    row per load, lanes of a row read consecutive 16-byte chunks, so a wave
-//    instruction moves whole 64-byte segments; all of a block's code and
-//    scale loads are issued before any arithmetic.
-//  * x stays in registers: the 4 waves of a block split K into quarters and a
-//    lane keeps the 64 x values of its chunk for every row it visits, so x
-//    is read from L2 once per block, not once per row.
-//  * Arithmetic is f32: a 2-bit code c (stored canonical, 0..2) becomes the
-//    float c - 1 exactly via the bit pattern 0x4B000000 | c (= 2^23 + c)
-//    minus 2^23 + 1; each lane sums its 64 products in f32, scales the chunk
-//    sum by the block's d once, and the per-row partials are reduced with
-//    cross-lane shuffles and a 4-wave LDS step.
+// Work split.  Lane t of a 256-thread block owns one 32-bit code word (16
+// consecutive k) of each of ROWS rows; LPS lanes (a power of two >= K/16,
+// at most 256) form a row slot, so a block covers 256/LPS slots x ROWS rows.
+// For K > 4096 a slot walks K in 4096-wide segments.  A wave therefore reads
+// 256 contiguous code bytes per row, and a lane keeps its 16 x values in
+// registers for all ROWS rows.
+//
+// Latency.  The code words and scales of all ROWS rows are loaded with
+// clamped, branch-free addresses before any arithmetic, so one block keeps
+// ROWS loads per lane in flight instead of paying the HBM latency per row.
+//
+// Arithmetic (f32 products and sums, weights exact).  One AND-OR puts two
+// codes of the word into the mantissas of a binary16 pair 1024 + 4^f c (the
+// SoA stores codes k and k+1 at bits 2f and 2f+16, see tq2_internal.h); one
+// packed FMA maps it to the exact pair (c - 1); each weight then costs one
+// v_fma_mix_f32 (f32 x times binary16 weight, f32 accumulate).  Each lane's
+// 16-term sum is scaled by its block's d once; the partial sums of a row are
+// added in LDS and with cross-lane shuffles, and the residual is added last.
 #include "tq2_internal.h"
 
 namespace tq2 {
 namespace {
 
-constexpr int kThreads = 256;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float code_minus_one(uint32_t c) {
-  return __uint_as_float(0x4B000000u | c) - 8388609.0f;
+constexpr int kThreads = 256;
+constexpr uint32_t kMagic = 0x64006400u;   // binary16 pair (1024, 1024)
+
+// v_and_or_b32 with the mask in an SGPR (gfx9 VOP3 takes no literal).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
 }
 
-// Sum over the 64 weights of one 16-byte chunk of  x[k] * (code(k) - 1).
-__device__ __forceinline__ float chunk_dot(const uint4& cw, const float (&xv)[64]) {
-  const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+// The 8 exact binary16 pairs (c_k - 1, c_{k+1} - 1) of one code word.
+__device__ __forceinline__ void decode_word(uint32_t w, uint32_t magic, half2_t (&v)[8]) {
+  const uint32_t w10 = w >> 10;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int f = p < 5 ? p : p - 5;          // field position inside the half-word
+    const uint32_t src = p < 5 ? w : w10;
+    const uint32_t mask = (3u << (2 * f)) | (3u << (2 * f + 16));
+    const half2_t h = __builtin_bit_cast(half2_t, and_or(src, mask, magic));
+    const _Float16 sc = _Float16(1.0f / float(1 << (2 * f)));
+    const _Float16 off = _Float16(-(1024.0f / float(1 << (2 * f)) + 1.0f));
+    const half2_t scv = {sc, sc};
+    const half2_t offv = {off, off};
+    v[p] = h * scv + offv;
+  }
+}
+
+__device__ __forceinline__ float dot16(const half2_t (&v)[8], const float (&xv)[16]) {
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t w = words[q];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      s0 = fmaf(xv[16 * q + 2 * p], code_minus_one((w >> (2 * p)) & 3u), s0);
-      s1 = fmaf(xv[16 * q + 2 * p + 1], code_minus_one((w >> (2 * p + 16)) & 3u), s1);
-    }
+  for (int p = 0; p < 8; ++p) {
+    s0 = __builtin_fmaf(xv[2 * p], float(v[p][0]), s0);
+    s1 = __builtin_fmaf(xv[2 * p + 1], float(v[p][1]), s1);
   }
   return s0 + s1;
 }
 
-// RPW rows per wave pass (64 / RPW lanes per row), PASSES passes per block.
-template <int RPW, int PASSES>
+// Load ROWS code words and scales of word wc, and the 16 x values of it.
+template <int ROWS>
+__device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
+                                             const uint16_t* __restrict__ scales,
+                                             const float* __restrict__ x, int row0, int n_rows,
+                                             int wpr, int kb_count, int wc, uint32_t (&cw)[ROWS],
+                                             uint32_t (&db)[ROWS], float (&xv)[16]) {
+  const unsigned uwc = unsigned(wc);            // lane offset: 32-bit, base pointer uniform
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int row = min(row0 + r, n_rows - 1);
+    const uint32_t* crow = codes + size_t(row) * wpr;
+    const uint16_t* srow = scales + size_t(row) * kb_count;
+    cw[r] = crow[uwc];
+    db[r] = srow[uwc >> 3];
+  }
+  const float4* xp = reinterpret_cast<const float4*>(x + 16 * wc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 q = xp[i];
+    xv[4 * i] = q.x;
+    xv[4 * i + 1] = q.y;
+    xv[4 * i + 2] = q.z;
+    xv[4 * i + 3] = q.w;
+  }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void accumulate_segment(const uint32_t (&cw)[ROWS],
+                                                   const uint32_t (&db)[ROWS],
+                                                   const float (&xv)[16], bool live,
+                                                   float (&part)[ROWS]) {
+  const uint32_t magic = kMagic;
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    half2_t v[8];
+    decode_word(cw[r], magic, v);
+    const float d = float(__builtin_bit_cast(_Float16, uint16_t(db[r])));
+    const float s = dot16(v, xv) * d;
+    part[r] += live ? s : 0.f;
+  }
+}
+
+// ONE_SEG: K/16 <= LPS, the whole row fits one pass and every load of the
+// thread is issued before the first use.
+template <int ROWS, int LPS, bool ONE_SEG>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint32_t* __restrict__ codes,
                                                         const uint16_t* __restrict__ scales,
                                                         const float* __restrict__ x,
                                                         const float* __restrict__ residual,
                                                         float* __restrict__ out, int n_rows,
                                                         int k) {
-  constexpr int LPR = 64 / RPW;
-  constexpr int R = RPW * PASSES;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int rs = lane / LPR;
-  const int lc = lane % LPR;
-  const int chunks = k >> 6;
+  constexpr int SLOTS = kThreads / LPS;
+  constexpr int OUTS = SLOTS * ROWS;            // rows per block
+  constexpr int G = kThreads / OUTS;            // threads that finish one row
+  static_assert(LPS >= ROWS && G >= 1 && G <= 64, "reduction shape");
+  const int t = threadIdx.x;
+  // With one slot per block the row indices are block-uniform (scalar).
+  const int slot = SLOTS == 1 ? 0 : t / LPS;
+  const int lw = SLOTS == 1 ? t : t % LPS;      // word index inside a K segment
+  const int wpr = k >> 4;                       // code words per row
   const int kb_count = k >> 7;
-  const int words_per_row = k >> 4;
-  const int row0 = blockIdx.x * R;
+  const int row0 = blockIdx.x * OUTS + slot * ROWS;
 
-  float acc[PASSES];
+  float part[ROWS];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) acc[p] = 0.f;
+  for (int r = 0; r < ROWS; ++r) part[r] = 0.f;
 
-  for (int seg = 0; seg < chunks; seg += 4 * LPR) {
-    const int j = seg + wave * LPR + lc;
-    const bool active = j < chunks;
-    uint4 cw[PASSES];
-    float dv[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = row0 + p * RPW + rs;
-      if (active && row < n_rows) {
-        cw[p] = *reinterpret_cast<const uint4*>(codes + size_t(row) * words_per_row + 4 * j);
-        const _Float16 d = __builtin_bit_cast(_Float16, scales[size_t(row) * kb_count + (j >> 1)]);
-        dv[p] = float(d);
-      } else {
-        cw[p] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
-        dv[p] = 0.f;
-      }
-    }
-    float xv[64];
-    if (active) {
-      const float4* xp = reinterpret_cast<const float4*>(x + 64 * j);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float4 v = xp[i];
-        xv[4 * i] = v.x;
-        xv[4 * i + 1] = v.y;
-        xv[4 * i + 2] = v.z;
-        xv[4 * i + 3] = v.w;
-      }
+  uint32_t cw[ROWS];
+  uint32_t db[ROWS];
+  float xv[16];
+  if constexpr (ONE_SEG) {
+    if (wpr == LPS) {                           // every lane has a word: no masking
+      load_segment<ROWS>(codes, scales, x, row0, n_rows, wpr, kb_count, lw, cw, db, xv);
+      accumulate_segment<ROWS>(cw, db, xv, true, part);
     } else {
-#pragma unroll
-      for (int i = 0; i < 64; ++i) xv[i] = 0.f;
+      const bool live = lw < wpr;
+      load_segment<ROWS>(codes, scales, x, row0, n_rows, wpr, kb_count, live ? lw : wpr - 1,
+                         cw, db, xv);
+      accumulate_segment<ROWS>(cw, db, xv, live, part);
     }
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) acc[p] = fmaf(chunk_dot(cw[p], xv), dv[p], acc[p]);
+  } else {
+    for (int seg = 0; seg < wpr; seg += LPS) {
+      const int w = seg + lw;
+      const bool live = w < wpr;
+      load_segment<ROWS>(codes, scales, x, row0, n_rows, wpr, kb_count, live ? w : wpr - 1, cw,
+                         db, xv);
+      accumulate_segment<ROWS>(cw, db, xv, live, part);
+    }
   }
 
+  // Row sums: red[r][t] holds thread t's partial of its slot's row r.
+  __shared__ float red[ROWS][kThreads];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc[p] += __shfl_xor(acc[p], off, 64);
-  }
-
-  __shared__ float red[4][R];
-  if (lc == 0) {
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) red[wave][p * RPW + rs] = acc[p];
-  }
+  for (int r = 0; r < ROWS; ++r) red[r][t] = part[r];
   __syncthreads();
-  if (threadIdx.x < R) {
-    const int row = row0 + threadIdx.x;
+  const int o = t / G;                          // block row finished by this thread
+  const int os = o / ROWS;                      // its slot
+  const int orr = o % ROWS;                     // its row inside the slot
+  const int g = t % G;
+  constexpr int PER = LPS / G;                  // partials summed by one thread
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v += red[orr][os * LPS + g * PER + i];
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  if (g == 0) {
+    const int row = blockIdx.x * OUTS + os * ROWS + orr;
     if (row < n_rows) {
-      float v = (red[0][threadIdx.x] + red[1][threadIdx.x]) +
-                (red[2][threadIdx.x] + red[3][threadIdx.x]);
       if (residual) v = residual[row] + v;
       out[row] = v;
     }
   }
 }
 
-template <int RPW>
-hipError_t launch_rpw(int passes, const uint32_t* codes, const uint16_t* scales, const float* x,
-                      const float* residual, float* out, int n, int k, hipStream_t stream) {
-  const int rows_per_block = RPW * passes;
-  const dim3 grid((n + rows_per_block - 1) / rows_per_block);
-  switch (passes) {
-    case 1:
-      hipLaunchKernelGGL((gemv_kernel<RPW, 1>), grid, dim3(kThreads), 0, stream, codes, scales,
-                         x, residual, out, n, k);
-      break;
-    case 2:
-      hipLaunchKernelGGL((gemv_kernel<RPW, 2>), grid, dim3(kThreads), 0, stream, codes, scales,
-                         x, residual, out, n, k);
-      break;
+template <int ROWS>
+hipError_t launch_rows(int lps, const uint32_t* codes, const uint16_t* scales, const float* x,
+                       const float* residual, float* out, int n, int k, hipStream_t stream) {
+  const int outs = (kThreads / lps) * ROWS;
+  const dim3 grid((n + outs - 1) / outs);
+#define TQ2_GEMV_CASE(L)                                                                     \
+  case L:                                                                                    \
+    hipLaunchKernelGGL((gemv_kernel<ROWS, L, true>), grid, dim3(kThreads), 0, stream, codes,   \
+                       scales, x, residual, out, n, k);                                      \
+    break;
+  switch (lps) {
+    TQ2_GEMV_CASE(8)
+    TQ2_GEMV_CASE(16)
+    TQ2_GEMV_CASE(32)
+    TQ2_GEMV_CASE(64)
+    TQ2_GEMV_CASE(128)
     default:
-      hipLaunchKernelGGL((gemv_kernel<RPW, 4>), grid, dim3(kThreads), 0, stream, codes, scales,
-                         x, residual, out, n, k);
+      if (k / 16 <= 256)
+        hipLaunchKernelGGL((gemv_kernel<ROWS, 256, true>), grid, dim3(kThreads), 0, stream, codes,
+                           scales, x, residual, out, n, k);
+      else
+        hipLaunchKernelGGL((gemv_kernel<ROWS, 256, false>), grid, dim3(kThreads), 0, stream,
+                           codes, scales, x, residual, out, n, k);
       break;
   }
+#undef TQ2_GEMV_CASE
   return hipGetLastError();
 }
 
@@ -154,25 +217,17 @@ hipError_t launch_gemv(const uint8_t* soa, const float* x, const float* residual
                        int64_t n, int64_t k, hipStream_t stream) {
   const uint32_t* codes = reinterpret_cast<const uint32_t*>(soa);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(soa + scales_offset(n, k));
-  // Lanes per row: enough 16-byte chunks for one quarter of K, a power of two, <= 64.
-  const int64_t chunks = k / 64;
-  const int64_t quarter = (chunks + 3) / 4;
-  int lpr = 1;
-  while (lpr < quarter && lpr < 64) lpr <<= 1;
-  const int rpw = 64 / lpr;
-  // Passes: keep at least ~512 blocks in flight where the row count allows.
-  int passes = 4;
-  while (passes > 1 && (n + int64_t(rpw) * passes - 1) / (int64_t(rpw) * passes) < 512) passes >>= 1;
+  const int64_t wpr = k / 16;
+  int lps = 8;
+  while (lps < wpr && lps < kThreads) lps <<= 1;
+  // Rows per thread: 8 when that still gives >= 2 blocks per CU, else fewer.
+  const int slots = kThreads / lps;
+  int rows = 8;
+  while (rows > 4 && (n + int64_t(slots) * rows - 1) / (int64_t(slots) * rows) < 512) rows >>= 1;
+  if (rows > lps) rows = lps;
   const int ni = int(n), ki = int(k);
-  switch (rpw) {
-    case 64: return launch_rpw<64>(passes, codes, scales, x, residual, out, ni, ki, stream);
-    case 32: return launch_rpw<32>(passes, codes, scales, x, residual, out, ni, ki, stream);
-    case 16: return launch_rpw<16>(passes, codes, scales, x, residual, out, ni, ki, stream);
-    case 8: return launch_rpw<8>(passes, codes, scales, x, residual, out, ni, ki, stream);
-    case 4: return launch_rpw<4>(passes, codes, scales, x, residual, out, ni, ki, stream);
-    case 2: return launch_rpw<2>(passes, codes, scales, x, residual, out, ni, ki, stream);
-    default: return launch_rpw<1>(passes, codes, scales, x, residual, out, ni, ki, stream);
-  }
+  if (rows == 8) return launch_rows<8>(lps, codes, scales, x, residual, out, ni, ki, stream);
+  return launch_rows<4>(lps, codes, scales, x, residual, out, ni, ki, stream);
 }
 
 }  // namespace tq2
