@@ -36,7 +36,34 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-chain", action="store_true",
+                   help="skip the 100-layer M=1536 chain (config 5)")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="also run one device-to-device copy of this size (MiB) so a "
+                        "counter run can scale FETCH_SIZE / WRITE_SIZE against known bytes")
     return p.parse_args()
+
+
+def measured_traffic(key, source):
+    """HBM bytes per launch of one kernel from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled against a device copy of known size), or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        with open(os.path.join(here, source), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+        with open(os.path.join(here, "profiles", "gemv_k4096_n4096_traffic.md")) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    tag = "machine-readable: %s=" % key
+    for line in lines:
+        if line.startswith(tag):
+            fields = dict(kv.split("=", 1) for kv in line[len("machine-readable: "):].split())
+            if fields.get("kernel_source_sha256") == digest:
+                return int(fields[key])
+    return None
 
 
 def gemv_bytes(n, k, residual):
@@ -89,6 +116,65 @@ def cpu_baseline(case, seconds):
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "%d full oracle evaluations of the K=N=4096 residual GEMV (float64 numpy "
                       "dequantize + product, 1 BLAS thread), %.3f s each" % (reps, dt)}
+
+
+def chain_bench(torch, tq2, G, dev, stream):
+    """Config 5: 100 chained ternary linears at M = 1536 (shapes repeating
+    3072->9216, 3072->3072, 3072->12288, 12288->3072), each with its own
+    seeded weight; after a 9216-wide layer the next layer takes the first 3072
+    columns, and every input is RMS-rescaled per row (plain torch glue).
+    Reported: the GEMM kernels alone (graph of the 100 GEMM launches on fixed
+    inputs) and the whole chain with the glue."""
+    m = G.CHAIN_M
+    soas, shapes = [], []
+    for layer in range(G.CHAIN_LAYERS):
+        k, n = G.chain_layer_shape(layer)
+        aos = torch.from_numpy(G.chain_layer_weight(layer)).to(dev)
+        soas.append(tq2.reformat_aos_to_soa(aos, n, k))
+        shapes.append((k, n))
+        del aos
+    x0 = torch.from_numpy(G.chain_input()).to(dev)
+    xs = {3072: x0.clone(), 12288: torch.randn((m, 12288), device=dev)}
+    outs = {n: torch.empty((m, n), dtype=torch.float32, device=dev) for n in (3072, 9216, 12288)}
+    flop = sum(2.0 * m * n * k for k, n in shapes)
+
+    def gemms_only(_):
+        for (k, n), soa in zip(shapes, soas):
+            st = tq2.gemm_ptr(soa.data_ptr(), xs[k].data_ptr(), 0, outs[n].data_ptr(), m, n, k,
+                              torch.cuda.current_stream(dev).cuda_stream)
+            if st != 0:
+                raise RuntimeError("tq2_gemm failed: %s" % tq2.status_string(st))
+
+    g = capture(torch, stream, gemms_only, 1)
+    time_graph(torch, g, 1, stream)
+    ms, _ = time_graph(torch, g, 3, stream)
+    kernels_ms = ms / 3
+
+    def full_chain():
+        x = x0
+        for layer, ((k, n), soa) in enumerate(zip(shapes, soas)):
+            y = tq2.gemm(soa, x, n, k)
+            nk = G.chain_layer_shape(layer + 1)[0]
+            y = y[:, :nk]
+            x = (y / torch.sqrt(torch.mean(y * y, dim=1, keepdim=True) + 1e-6)).contiguous()
+        return x
+
+    with torch.cuda.stream(stream):
+        full_chain()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        full_chain()
+        end.record(stream)
+    torch.cuda.synchronize()
+    chain_ms = start.elapsed_time(end)
+    del soas
+    return {"layers": G.CHAIN_LAYERS, "tflop": round(flop / 1e12, 4),
+            "gemm_kernels_ms": round(kernels_ms, 4),
+            "gemm_tflops": round(flop / (kernels_ms * 1e-3) / 1e12, 2),
+            "gemm_frac": round(flop / (kernels_ms * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
+            "with_glue_ms": round(chain_ms, 4)}
 
 
 def main():
@@ -157,8 +243,11 @@ def main():
                    "m": 1, "n": n, "k": k, "bytes_per_call": nbytes,
                    "wall_s_timed": round(wall, 4)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_kernel", "us_per_launch": round(us_per_call, 3)},
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("gemv_traffic_bytes_per_launch",
+                                                 "gemv_tq2_g128_amd/csrc/tq2_gemv.hip"),
+                     "traffic_unit": "bytes per launch", "kernel": "gemv_kernel",
+                     "us_per_launch": round(us_per_call, 3)},
     }
 
     # ---- large-M GEMM, M = 1536, K = N = 3072 --------------------------------
@@ -185,7 +274,21 @@ def main():
         result["gemm_m1536_k3072_n3072"] = {
             "tflops": round(tflops, 2), "us_per_call": round(us4, 3),
             "peak_tflops": F16_MFMA_PEAK_TFLOPS, "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
-            "path": tq2.gemm_path(m4, n4, k4), "calls": reps * per_graph}
+            "path": tq2.gemm_path(m4, n4, k4), "calls": reps * per_graph,
+            "traffic": measured_traffic("gemm_traffic_bytes_per_launch",
+                                        "gemv_tq2_g128_amd/csrc/tq2_gemm.hip")}
+
+    if not args.no_chain:
+        result["chain_100_layers_m1536"] = chain_bench(torch, tq2, G, dev, stream)
+
+    if args.calibrate_copy_mib > 0:
+        nb = args.calibrate_copy_mib * 2 ** 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = nb
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)

@@ -113,6 +113,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   static_assert((MT * (kChunk / 4)) % THREADS == 0, "A staging split");
 
   __shared__ _Float16 As[2][LIMBS][MT][kLdsRow];
+  // Weight ring: three chunks of codes (64 bytes per column) and scales
+  // (two binary16 per column), filled by direct-to-LDS loads two chunks ahead.
+  // A 2-byte direct-to-LDS load writes its value zero-extended to a dword at
+  // lane * 4, so each scale occupies a dword of the ring.
+  constexpr int kWSlots = 3;
+  __shared__ __attribute__((aligned(16))) uint8_t Wc[kWSlots][NT][64];
+  __shared__ __attribute__((aligned(16))) uint32_t Ws[kWSlots][NT][2];
 
   // XCD-aware tile order: block id b runs on XCD b % 8; give each XCD a
   // contiguous range of logical tiles (N-tiles of one M row-block adjacent).
@@ -144,11 +151,6 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   // codes and zero scales.
   const uint32_t aoff = uint32_t(tid >> 6) * uint32_t(K) * 4u + 16u * uint32_t(tid & 63);
   constexpr int AROWS = THREADS / 64;    // A rows staged per load instruction
-  const uint32_t nl = uint32_t(n0 + wn * NW + col);
-  const uint32_t coff = nl * uint32_t(K / 4) + 16u * g + 4u * QW * wk;
-  const uint32_t soff = (nl * uint32_t(KB) + uint32_t(g >> 1)) * 2u;
-  const int cstep = 16 * (K / 4);        // bytes between 16-column groups
-  const int sstep = 16 * KB * 2;
 
   typedef uint32_t codes_t[QW];
   auto load_a = [&](int c, float4 (&areg)[AV]) {
@@ -175,17 +177,43 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
       }
     }
   };
-  auto load_w = [&](int c, codes_t (&cwo)[CG], uint32_t (&dwo)[CG]) {
+
+  // Direct-to-LDS weight loads of chunk c into ring slot c % 3.  One wave
+  // instruction moves 16 columns of codes (64 lanes x 16 bytes) or 32
+  // columns of scales (64 lanes x one 2-byte scale each, stored as a dword);
+  // the block's waves share the instructions.
+  constexpr int CODE_INSTS = NT / 16;
+  constexpr int SCALE_INSTS = NT / 32;
+  static_assert(NT % 32 == 0, "weight ring split");
+  const uint32_t code_voff =
+      uint32_t(n0 + (lane >> 2)) * uint32_t(K / 4) + 16u * uint32_t(lane & 3);
+  const uint32_t scale_voff =
+      (uint32_t(n0 + (lane >> 1)) * uint32_t(KB) + uint32_t(lane & 1)) * 2u;
+  auto load_w = [&](int c) {
+    const int slot = c % kWSlots;
+    for (int q = wave; q < CODE_INSTS + SCALE_INSTS; q += THREADS / 64) {
+      if (q < CODE_INSTS) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rc, (__attribute__((address_space(3))) void*)&Wc[slot][16 * q][0], 16, code_voff,
+            q * 16 * (K / 4) + c * 64, 0, 0);
+      } else {
+        const int qs = q - CODE_INSTS;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)&Ws[slot][32 * qs][0], 2, scale_voff,
+            qs * 32 * KB * 2 + c * 4, 0, 0);
+      }
+    }
+  };
+  // This wave's codes and raw scale bits of chunk c, from the ring.
+  auto read_w = [&](int c, codes_t (&cw)[CG], uint32_t (&draw)[CG]) {
+    const int slot = c % kWSlots;
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      if constexpr (QW == 4) {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, coff, j * cstep + c * 64, 0);
-        cwo[j][0] = v[0]; cwo[j][1] = v[1]; cwo[j][2] = v[2]; cwo[j][3] = v[3];
-      } else {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, coff, j * cstep + c * 64, 0);
-        cwo[j][0] = v[0]; cwo[j][1] = v[1];
-      }
-      dwo[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, j * sstep + c * 4, 0);
+      const int nloc = wn * NW + j * 16 + col;
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(&Wc[slot][nloc][16 * g + 4 * QW * wk]);
+#pragma unroll
+      for (int q = 0; q < QW; ++q) cw[j][q] = p[q];
+      draw[j] = Ws[slot][nloc][g >> 1];
     }
   };
 
@@ -221,7 +249,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
       for (int l = 0; l < LIMBS; ++l)
 #pragma unroll
         for (int j = 0; j < CG; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i][l], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j], a[i][l], acc[i][j], 0, 0, 0);
   };
   // Ask the scheduler to interleave one step's MFMAs with the next step's
   // operand work: per MFMA about VALU/MFMA decode instructions and an LDS
@@ -270,32 +298,27 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
     }
   };
 
-  // ---- software pipeline: loads run one chunk ahead of the MFMAs ---------
+  // ---- software pipeline -------------------------------------------------
+  // x runs one chunk ahead (registers, then LDS); weights run two chunks
+  // ahead through the LDS ring.  Within an iteration the A loads are issued
+  // before the weight loads, so the wait for this iteration's A loads also
+  // covers the previous iteration's weight loads, and the barrier publishes
+  // both.
   float4 areg[AV];
-  codes_t cw[CG];
-  uint32_t draw[CG];
+  load_w(0);
   load_a(0, areg);
-  load_w(0, cw, draw);
+  if (nchunks > 1) load_w(1);
   store_a(0, areg);
+  __builtin_amdgcn_s_waitcnt(0);             // weight slots 0 and 1 have landed
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
-    codes_t cwn[CG];
-    uint32_t drawn[CG];
-    if (more) {
-      load_a(c + 1, areg);
-      load_w(c + 1, cwn, drawn);
-    }
+    if (c + 1 < nchunks) load_a(c + 1, areg);
+    if (c + 2 < nchunks) load_w(c + 2);
+    codes_t cw[CG];
+    uint32_t draw[CG];
+    read_w(c, cw, draw);
     compute(c, c & 1, cw, draw);
-    if (more) {
-      store_a((c & 1) ^ 1, areg);
-#pragma unroll
-      for (int j = 0; j < CG; ++j) {
-#pragma unroll
-        for (int q = 0; q < QW; ++q) cw[j][q] = cwn[j][q];
-        draw[j] = drawn[j];
-      }
-    }
+    if (c + 1 < nchunks) store_a((c & 1) ^ 1, areg);
     __syncthreads();
   }
 
@@ -323,21 +346,35 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
           acc[i][j][e] += red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane];
   }
 
-  // ---- epilogue: D[row = 4g + e][col] of each 16x16 tile -----------------
+  // ---- epilogue ------------------------------------------------------------
+  // The weight operand is the MFMA's first (row) operand, so each 16x16
+  // result holds D[n = 4g + e][m = col]: a lane owns four consecutive output
+  // columns of one row and writes them (and reads the residual) as one
+  // 16-byte access when the row pitch allows it.
+  const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < RT; ++i) {
+    const int m = m0 + i * 16 + col;
+    if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const int n = n0 + wn * NW + j * 16 + col;
-      if (n >= N) continue;
+      const int n = n0 + wn * NW + j * 16 + 4 * g;
+      const size_t o = size_t(m) * N + n;
+      if (vec && n + 3 < N) {
+        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        if (residual) {
+          const float4 r = *reinterpret_cast<const float4*>(residual + o);
+          v = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
+        }
+        *reinterpret_cast<float4*>(out + o) = v;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + i * 16 + 4 * g + e;
-        if (m < M) {
-          float v = acc[i][j][e];
-          const size_t o = size_t(m) * N + n;
-          if (residual) v = residual[o] + v;
-          out[o] = v;
+        for (int e = 0; e < 4; ++e) {
+          if (n + e < N) {
+            float v = acc[i][j][e];
+            if (residual) v = residual[o + e] + v;
+            out[o + e] = v;
+          }
         }
       }
     }
