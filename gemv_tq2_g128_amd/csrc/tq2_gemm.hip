@@ -80,6 +80,13 @@ __device__ __forceinline__ half8_t decode_step(uint32_t word, half2_t d2, uint32
   return b;
 }
 
+// Wait for this wave's LDS accesses, then join the workgroup barrier.  The
+// asm's memory clobber keeps the compiler from moving memory accesses across
+// it; unlike __syncthreads() it leaves the wave's global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -113,13 +120,6 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   static_assert((MT * (kChunk / 4)) % THREADS == 0, "A staging split");
 
   __shared__ _Float16 As[2][LIMBS][MT][kLdsRow];
-  // Weight ring: three chunks of codes (64 bytes per column) and scales
-  // (two binary16 per column), filled by direct-to-LDS loads two chunks ahead.
-  // A 2-byte direct-to-LDS load writes its value zero-extended to a dword at
-  // lane * 4, so each scale occupies a dword of the ring.
-  constexpr int kWSlots = 3;
-  __shared__ __attribute__((aligned(16))) uint8_t Wc[kWSlots][NT][64];
-  __shared__ __attribute__((aligned(16))) uint32_t Ws[kWSlots][NT][2];
 
   // XCD-aware tile order: block id b runs on XCD b % 8; give each XCD a
   // contiguous range of logical tiles (N-tiles of one M row-block adjacent).
@@ -139,6 +139,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   const int col = lane & 15;
   const int g = lane >> 4;
   const int KB = K >> 7;
+  typedef uint32_t codes_t[QW];
   const int nchunks = (K + kChunk - 1) / kChunk;
 
   // x rows m0 .. m0+MT-1 (rows past M read as zero).
@@ -152,7 +153,6 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   const uint32_t aoff = uint32_t(tid >> 6) * uint32_t(K) * 4u + 16u * uint32_t(tid & 63);
   constexpr int AROWS = THREADS / 64;    // A rows staged per load instruction
 
-  typedef uint32_t codes_t[QW];
   auto load_a = [&](int c, float4 (&areg)[AV]) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
@@ -178,42 +178,27 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
     }
   };
 
-  // Direct-to-LDS weight loads of chunk c into ring slot c % 3.  One wave
-  // instruction moves 16 columns of codes (64 lanes x 16 bytes) or 32
-  // columns of scales (64 lanes x one 2-byte scale each, stored as a dword);
-  // the block's waves share the instructions.
-  constexpr int CODE_INSTS = NT / 16;
-  constexpr int SCALE_INSTS = NT / 32;
-  static_assert(NT % 32 == 0, "weight ring split");
-  const uint32_t code_voff =
-      uint32_t(n0 + (lane >> 2)) * uint32_t(K / 4) + 16u * uint32_t(lane & 3);
-  const uint32_t scale_voff =
-      (uint32_t(n0 + (lane >> 1)) * uint32_t(KB) + uint32_t(lane & 1)) * 2u;
-  auto load_w = [&](int c) {
-    const int slot = c % kWSlots;
-    for (int q = wave; q < CODE_INSTS + SCALE_INSTS; q += THREADS / 64) {
-      if (q < CODE_INSTS) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rc, (__attribute__((address_space(3))) void*)&Wc[slot][16 * q][0], 16, code_voff,
-            q * 16 * (K / 4) + c * 64, 0, 0);
-      } else {
-        const int qs = q - CODE_INSTS;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)&Ws[slot][32 * qs][0], 2, scale_voff,
-            qs * 32 * KB * 2 + c * 4, 0, 0);
-      }
-    }
-  };
-  // This wave's codes and raw scale bits of chunk c, from the ring.
-  auto read_w = [&](int c, codes_t (&cw)[CG], uint32_t (&draw)[CG]) {
-    const int slot = c % kWSlots;
+  // Weight loads of chunk c straight into registers: each lane takes the
+  // QW code dwords of its column and k-group that this wave's steps use, and
+  // the raw binary16 scale of the block they fall in.  Columns past N read as
+  // zero codes and zero scales.
+  const uint32_t nl = uint32_t(n0 + wn * NW + col);
+  const uint32_t code_voff = nl * uint32_t(K / 4) + 16u * uint32_t(g) + 4u * QW * uint32_t(wk);
+  const uint32_t scale_voff = (nl * uint32_t(KB) + uint32_t(g >> 1)) * 2u;
+  auto load_w = [&](int c, codes_t (&cw)[CG], _Float16 (&dsc)[CG]) {
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const int nloc = wn * NW + j * 16 + col;
-      const uint32_t* p = reinterpret_cast<const uint32_t*>(&Wc[slot][nloc][16 * g + 4 * QW * wk]);
-#pragma unroll
-      for (int q = 0; q < QW; ++q) cw[j][q] = p[q];
-      draw[j] = Ws[slot][nloc][g >> 1];
+      if constexpr (QW == 4) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, code_voff,
+                                                                j * 16 * (K / 4) + c * 64, 0);
+        cw[j][0] = v[0]; cw[j][1] = v[1]; cw[j][2] = v[2]; cw[j][3] = v[3];
+      } else {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, code_voff,
+                                                               j * 16 * (K / 4) + c * 64, 0);
+        cw[j][0] = v[0]; cw[j][1] = v[1];
+      }
+      dsc[j] = __builtin_bit_cast(
+          _Float16, __builtin_amdgcn_raw_buffer_load_b16(rs, scale_voff, j * 16 * KB * 2 + c * 4, 0));
     }
   };
 
@@ -233,13 +218,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
       for (int l = 0; l < LIMBS; ++l)
         a[i][l] = *reinterpret_cast<const half8_t*>(&As[buf][l][i * 16 + col][64 * g + 8 * s]);
   };
-  auto decode_bfrags = [&](int ss, const codes_t (&cw)[CG], const uint32_t (&dw)[CG],
+  auto decode_bfrags = [&](int ss, const codes_t (&cw)[CG], const half2_t (&d2)[CG],
                            half8_t (&b)[CG]) {
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
       uint32_t w = cw[j][ss >> 1];
       if (ss & 1) w >>= 8;
-      b[j] = decode_step(w, as_half2(dw[j]), magic);
+      b[j] = decode_step(w, d2[j], magic);
     }
   };
   auto mfmas = [&](const half8_t (&a)[RT][LIMBS], const half8_t (&b)[CG]) {
@@ -266,12 +251,15 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
     }
   };
 
-  auto compute = [&](int c, int buf, const codes_t (&cw)[CG], const uint32_t (&draw)[CG]) {
+  auto compute = [&](int c, int buf, const codes_t (&cw)[CG], const _Float16 (&dsc)[CG]) {
     // binary16 pair (d, d), or (0, 0) where k runs past K in the last chunk.
     const bool live = c * kChunk + 64 * g < K;
-    uint32_t dw[CG];
+    half2_t dw[CG];
 #pragma unroll
-    for (int j = 0; j < CG; ++j) dw[j] = live ? (draw[j] | (draw[j] << 16)) : 0u;
+    for (int j = 0; j < CG; ++j) {
+      const _Float16 d = live ? dsc[j] : _Float16(0.0f);
+      dw[j] = half2_t{d, d};
+    }
     half8_t a0[RT][LIMBS], a1[RT][LIMBS], b0[CG], b1[CG];
     load_afrags(buf, wk * STEPS, a0);
     decode_bfrags(0, cw, dw, b0);
@@ -299,27 +287,33 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   };
 
   // ---- software pipeline -------------------------------------------------
-  // x runs one chunk ahead (registers, then LDS); weights run two chunks
-  // ahead through the LDS ring.  Within an iteration the A loads are issued
-  // before the weight loads, so the wait for this iteration's A loads also
-  // covers the previous iteration's weight loads, and the barrier publishes
-  // both.
+  // Iteration c computes chunk c from A buffer c % 2 and weight register set
+  // c % 2.  At its start it converts and stores x chunk c + 1 (loaded during
+  // iteration c - 1) and issues the loads of x chunk c + 2; after its MFMAs it
+  // loads weight chunk c + 2 into the register set it has just used.  Every
+  // load therefore has a whole iteration to land.  The loads are issued even
+  // past the last chunk (the buffer resources return zeros out of range, and
+  // the values are never used) so that every iteration has the same number
+  // of loads in flight and the compiler's wait counts stay exact.  The
+  // closing barrier only waits for this wave's LDS stores (a plain
+  // s_barrier: __syncthreads()'s fence would also drain the loads in flight).
   float4 areg[AV];
-  load_w(0);
-  load_a(0, areg);
-  if (nchunks > 1) load_w(1);
-  store_a(0, areg);
-  __builtin_amdgcn_s_waitcnt(0);             // weight slots 0 and 1 have landed
-  __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) load_a(c + 1, areg);
-    if (c + 2 < nchunks) load_w(c + 2);
-    codes_t cw[CG];
-    uint32_t draw[CG];
-    read_w(c, cw, draw);
-    compute(c, c & 1, cw, draw);
-    if (c + 1 < nchunks) store_a((c & 1) ^ 1, areg);
-    __syncthreads();
+  codes_t cw0[CG], cw1[CG];
+  _Float16 dr0[CG], dr1[CG];
+  // The loop starts at c = -2 (the first two passes only fill the pipeline)
+  // and always runs both passes of a pair (a pass past the last chunk only
+  // issues loads), so every pass issues the same loads in the same place and
+  // the wait counts the compiler derives hold on every path through the loop.
+  auto iteration = [&](int c, codes_t (&cw)[CG], _Float16 (&dsc)[CG]) {
+    if (c + 1 >= 0 && c + 1 < nchunks) store_a((c + 1) & 1, areg);
+    load_a(c + 2, areg);
+    if (c >= 0 && c < nchunks) compute(c, c & 1, cw, dsc);
+    load_w(c + 2, cw, dsc);
+    lds_barrier();
+  };
+  for (int c = -2; c < nchunks; c += 2) {
+    iteration(c, cw0, dr0);
+    iteration(c + 1, cw1, dr1);
   }
 
   // ---- K-split reduction: the wk = 1 waves hand their sums to wk = 0 -----

@@ -47,9 +47,10 @@ hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float
 // Largest M served by the split-f16 (f32-class) matrix-core path.
 constexpr int64_t kSplitMaxM = 16;
 
-// The matrix-core kernels address x row blocks and the weight planes through
-// 32-bit buffer offsets: K <= 2^22 and N * K / 4 < 2^31 bytes of codes.
-constexpr int64_t kGemmMaxK = int64_t(1) << 22;
+// The matrix-core kernels address x row blocks (up to 128 rows of K f32) and
+// the weight planes through 32-bit buffer offsets: K <= 2^21 and
+// N * K / 4 < 2^31 bytes of codes.
+constexpr int64_t kGemmMaxK = int64_t(1) << 21;
 constexpr int64_t kGemmMaxCodeBytes = int64_t(1) << 31;
 
 }  // namespace tq2
