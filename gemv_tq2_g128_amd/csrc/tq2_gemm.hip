@@ -5,22 +5,23 @@
 // `MetalPipelines`, ternary section): v8 decodes each weight block once per
 // M-tile; v9 drives the matrix units with f16-staged operands and f32
 // accumulation; v10 stages the dequantised weight as binary16 -- exact, since
-// code * d is +-d or 0 -- and double-buffers the K staging.  This kernel keeps
-// those properties and lays the work out for gfx950:
+// code * d is +-d or 0 -- and double-buffers the K staging.  These kernels
+// keep those properties and lay the work out for gfx950:
 //
-//  * v_mfma_f32_16x16x32_f16, one wave per SIMD, 4 waves per block.  A block
-//    owns an MT x (4*NW) output tile; each wave owns MT rows x NW columns.
-//  * x (f32) is staged through LDS once per block per 256-wide K chunk,
-//    converted to binary16 with round-to-nearest-even on the way in, double
-//    buffered so the next chunk's global loads overlap the current MFMAs.
-//  * Weights go straight from the SoA codes to MFMA operand registers: a lane
-//    reads 16 code bytes (64 weights of one column) per chunk and decodes them
-//    into exact binary16 (c - 1) * d with an AND-OR into the mantissa of a
-//    binary16 pair, one packed FMA and one packed multiply.  Each weight is
-//    decoded once per block and never touches LDS.
-//  * LIMBS = 2 is the f32-class variant for small M: x = hi + lo with
-//    hi = f16(x), lo = f16(x - hi); both parts hit the same exact weight
-//    operand and accumulate in f32 (relative error of x about 2^-22).
+//  * v_mfma_f32_16x16x32_f16 with the weight as the first operand, 64-wide
+//    waves, 8 waves per block (two per SIMD).  Each wave owns MT rows x NW
+//    columns of the block tile and half of the MFMA steps of each 256-wide K
+//    chunk; the two halves' partial sums meet in LDS at the end.
+//  * x (f32) is loaded a chunk ahead into registers, converted to binary16
+//    with round-to-nearest-even and stored into a double-buffered LDS tile.
+//  * Weights go from the SoA code words straight into MFMA operand registers:
+//    one AND-OR into the mantissa of a binary16 pair, one packed FMA and one
+//    packed multiply give the exact binary16 (c - 1) * d of two weights.
+//    Each weight is decoded once per block and never touches LDS.
+//  * LIMBS = 2 (small M) splits x = hi + lo into two binary16 parts that hit
+//    the same exact weight operand: f32-class accuracy (about 2^-22).
+//  * gemm_pp_kernel (large M) runs its two wave groups half a chunk apart:
+//    one group issues MFMAs while the other decodes, converts and loads.
 //  * Blocks are numbered so that the N-tiles of the same M rows land on the
 //    same XCD (the dispatcher deals block ids round-robin over 8 XCDs): x, at
 //    4 bytes per element, is the costly operand to re-fetch, so an XCD's L2
@@ -44,6 +45,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kChunk = 256;            // k per pipeline stage
 constexpr int kLdsRow = kChunk + 8;    // binary16 per LDS row (16-byte pad vs bank conflicts)
+constexpr int kPpMaxKB = 96;           // scale blocks per row the ping-pong kernel keeps in LDS (K <= 12288)
 
 __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
@@ -375,6 +377,321 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong variant for large M.  Eight waves, two groups of four; wave w and
+// wave w + 4 share a SIMD.  Both groups own the same MT x 4NW output tile and
+// the same columns per wave (wn = w & 3); group p takes MFMA steps 4p .. 4p+3
+// of every 256-wide chunk.  The groups run half a chunk apart: while one group
+// issues its chunk's 72 MFMAs (at raised wave priority, operands ready:
+// weights decoded beforehand into registers, x fragments read from LDS one
+// step ahead), the other group does the memory work -- decodes its weights
+// for its next MFMA phase, converts and stores its half of the next x tile,
+// and issues the global loads one chunk ahead.  A barrier separates the
+// phases, so each SIMD's matrix core alternates between its two waves while
+// the VALU, LDS and load path work for the other.
+//
+// Phase order (chunk c):  A: group 0 MFMA(c), group 1 MEM;  B: group 1
+// MFMA(c), group 0 MEM.  x tile c + 1 is stored in two halves, by group 1 in
+// phase A and by group 0 in phase B, into the buffer nobody reads during
+// chunk c.
+template <int MT, int NW>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ x,
+                                                      const float* __restrict__ residual,
+                                                      float* __restrict__ out, int M, int N, int K,
+                                                      int tiles_m, int tiles_n) {
+  constexpr int GT = 256;                // threads per group
+  constexpr int RT = MT / 16;
+  constexpr int CG = NW / 16;
+  constexpr int NT = 4 * NW;
+  constexpr int STEPS = 4;               // MFMA steps per group per chunk
+  constexpr int QW = 2;                  // code dwords per lane per chunk
+  constexpr int AV = MT * (kChunk / 4) / 2 / GT;   // float4 of x per thread per chunk
+  static_assert(MT % 32 == 0 && NW % 16 == 0, "tile shape");
+  static_assert((MT / 2) * (kChunk / 4) % GT == 0, "x staging split");
+
+  __shared__ _Float16 As[2][MT][kLdsRow];
+  // The block's scales for the whole K (NT rows of the scales plane, which
+  // are contiguous), loaded once.
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[NT * kPpMaxKB];
+
+  const int ntiles = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  const int mt = t / tiles_n;
+  const int nt = t - mt * tiles_n;
+  const int m0 = mt * MT;
+  const int n0 = nt * NT;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int grp = wave >> 2;
+  const int wn = wave & 3;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int gt = tid & (GT - 1);         // thread index inside the group
+  const int KB = K >> 7;
+  const int nchunks = (K + kChunk - 1) / kChunk;
+
+  const rsrc_t rx = make_rsrc(x + size_t(m0) * K, uint32_t(min(MT, M - m0)) * uint32_t(K) * 4u);
+  const rsrc_t rc = make_rsrc(codes, uint32_t(N) * uint32_t(K / 4));
+  const rsrc_t rs = make_rsrc(scales, uint32_t(N) * uint32_t(KB) * 2u);
+
+  // x staging: group p converts rows p*MT/2 .. p*MT/2 + MT/2 - 1 of a chunk;
+  // its thread gt handles float4 f = gt + GT*i: row f / 64, float4 f % 64.
+  constexpr int AROWS = GT / 64;
+  const int arow0 = grp * (MT / 2) + (gt >> 6);
+  const uint32_t aoff = uint32_t(arow0) * uint32_t(K) * 4u + 16u * uint32_t(gt & 63);
+  float4 areg[AV];
+  auto load_a = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, aoff, i * AROWS * K * 4 + c * kChunk * 4, 0);
+      areg[i] = __builtin_bit_cast(float4, v);
+    }
+  };
+  auto store_a = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+      const float4 v = areg[i];
+      half4_t h = {_Float16(v.x), _Float16(v.y), _Float16(v.z), _Float16(v.w)};
+      *reinterpret_cast<half4_t*>(&As[buf][arow0 + AROWS * i][4 * (gt & 63)]) = h;
+    }
+  };
+
+  // Weights: lane's column, its k-group g, this group's half of the steps.
+  const uint32_t nl = uint32_t(n0 + wn * NW + col);
+  const uint32_t code_voff = nl * uint32_t(K / 4) + 16u * uint32_t(g) + 4u * QW * uint32_t(grp);
+  uint32_t cw[CG][QW];
+  auto load_w = [&](int c) {
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, code_voff,
+                                                             j * 16 * (K / 4) + c * 64, 0);
+      cw[j][0] = v[0];
+      cw[j][1] = v[1];
+    }
+  };
+  // Scale of this lane's column j and chunk c: block 2c + (g >> 1).  The
+  // chunk is clamped so the read stays inside Ls for the pass past the end;
+  // with an odd block count the last chunk's second block reads the next
+  // row's first scale (still inside Ls, since KB < kPpMaxKB), and the caller
+  // zeroes it.
+  const int ls_base = (wn * NW + col) * KB + (g >> 1);
+  auto scale_of = [&](int j, int c) {
+    return __builtin_bit_cast(_Float16, Ls[ls_base + j * 16 * KB + 2 * min(c, nchunks - 1)]);
+  };
+
+  // Decoded weight operands of one MFMA phase.  The memory phase decodes
+  // steps 0 .. STEPS-2 and keeps the code word and scale pair of the last
+  // step, which the MFMA phase decodes itself between its MFMAs (one column
+  // group per step), so that the two phases carry similar VALU work.
+  const uint32_t magic = 0x64006400u;
+  half8_t bf[STEPS][CG];
+  uint32_t wlast[CG];
+  half2_t dlast[CG];
+  auto decode_all = [&](int c) {
+    const bool live = c * kChunk + 64 * g < K && c < nchunks;
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const _Float16 d = live ? scale_of(j, c) : _Float16(0.0f);
+      const half2_t d2 = {d, d};
+#pragma unroll
+      for (int ss = 0; ss < STEPS - 1; ++ss) {
+        uint32_t w = cw[j][ss >> 1];
+        if (ss & 1) w >>= 8;
+        bf[ss][j] = decode_step(w, d2, magic);
+      }
+      wlast[j] = cw[j][(STEPS - 1) >> 1] >> 8;
+      dlast[j] = d2;
+    }
+  };
+
+  floatx4_t acc[RT][CG];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < CG; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto load_afrags = [&](int buf, int s, half8_t (&a)[RT]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      a[i] = *reinterpret_cast<const half8_t*>(&As[buf][i * 16 + col][64 * g + 8 * s]);
+  };
+  auto mfmas = [&](const half8_t (&a)[RT], const half8_t (&b)[CG]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CG; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+  // MFMA phase: x fragments of step ss + 1 are read while step ss's MFMAs
+  // issue (one LDS read per CG MFMAs), so every read has a step to land.
+  auto mfma_phase = [&](int c) {
+    const int buf = c & 1;
+    __builtin_amdgcn_s_setprio(1);
+    half8_t a0[RT], a1[RT];
+    load_afrags(buf, grp * STEPS, a0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ss = 0; ss < STEPS; ++ss) {
+      if ((ss & 1) == 0) {
+        if (ss + 1 < STEPS) load_afrags(buf, grp * STEPS + ss + 1, a1);
+        mfmas(a0, bf[ss]);
+      } else {
+        if (ss + 1 < STEPS) load_afrags(buf, grp * STEPS + ss + 1, a0);
+        mfmas(a1, bf[ss]);
+      }
+      // Last step's operands, one column group per earlier step.
+#pragma unroll
+      for (int j = 0; j < CG; ++j)
+        if (ss == (j * (STEPS - 1)) / CG) bf[STEPS - 1][j] = decode_step(wlast[j], dlast[j], magic);
+#pragma unroll
+      for (int q = 0; q < RT * CG; ++q) {
+        if (q % CG == 0 && ss + 1 < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (ss + 1 < STEPS) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Pin the decoded operands (and so all decode arithmetic) before the
+  // barrier that ends a memory phase; register-only work could otherwise
+  // drift past it into the MFMA phase.
+  auto pin_operands = [&]() {
+#pragma unroll
+    for (int ss = 0; ss < STEPS - 1; ++ss)
+#pragma unroll
+      for (int j = 0; j < CG; ++j) asm volatile("" ::"v"(bf[ss][j]));
+#pragma unroll
+    for (int j = 0; j < CG; ++j) asm volatile("" ::"v"(wlast[j]), "v"(dlast[j]));
+  };
+  // Memory phase: decode chunk cd's weights (registers loaded one chunk ago),
+  // store this group's half of x chunk cs, then reload the registers with x
+  // chunk cs + 1 and weight chunk cw_next.
+  auto mem_phase = [&](int cd, int cs, int cw_next) {
+    decode_all(cd);
+    store_a(cs & 1);
+    load_a(cs + 1);
+    load_w(cw_next);
+    pin_operands();
+  };
+
+  // Prologue: the block's scales into LDS; x tile 0 complete in buffer 0;
+  // group 0's operands for chunk 0 decoded and its weights of chunk 1 in
+  // flight; group 1 holds chunk 0's weights.  Both hold their half of x
+  // chunk 1 in registers.
+  {
+    // 16-byte loads for the whole granules (a load that straddles the end
+    // of a buffer resource returns zeros in full), 2-byte loads for the tail.
+    // Entries for columns past N are left unset: their outputs are never
+    // stored.
+    const uint32_t valid = uint32_t(min(NT, N - n0)) * uint32_t(KB) * 2u;
+    const uint32_t full = valid & ~15u;
+    const rsrc_t rsb = make_rsrc(scales + size_t(n0) * KB * 2, valid);
+    for (uint32_t o = 16u * uint32_t(tid); o < full; o += 16u * 512u) {
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsb, o, 0, 0);
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(Ls) + o) = v;
+    }
+    const uint32_t o2 = full + 2u * uint32_t(tid);
+    if (o2 < valid) Ls[o2 >> 1] = __builtin_amdgcn_raw_buffer_load_b16(rsb, o2, 0, 0);
+  }
+  load_a(0);
+  load_w(0);
+  store_a(0);
+  load_a(1);
+  lds_barrier();                         // scales visible
+  if (grp == 0) {
+    decode_all(0);
+    load_w(1);
+    pin_operands();
+  }
+  lds_barrier();
+  if (grp == 0) {
+    for (int c = 0; c < nchunks; ++c) {
+      mfma_phase(c);
+      lds_barrier();
+      mem_phase(c + 1, c + 1, c + 2);
+      lds_barrier();
+    }
+  } else {
+    for (int c = 0; c < nchunks; ++c) {
+      mem_phase(c, c + 1, c + 1);
+      lds_barrier();
+      mfma_phase(c);
+      lds_barrier();
+    }
+  }
+
+  // ---- group 1 hands its partial sums to group 0 --------------------------
+  float* red = reinterpret_cast<float*>(&As[0][0][0]);
+  static_assert(4 * RT * CG * 4 * 64 * 4 <= sizeof(As), "reduction buffer");
+  if (grp == 1) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CG; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+  }
+  __syncthreads();
+  if (grp == 1) return;
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < CG; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[i][j][e] += red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane];
+
+  const bool vec = (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < RT; ++i) {
+    const int m = m0 + i * 16 + col;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const int n = n0 + wn * NW + j * 16 + 4 * g;
+      const size_t o = size_t(m) * N + n;
+      if (vec && n + 3 < N) {
+        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        if (residual) {
+          const float4 r = *reinterpret_cast<const float4*>(residual + o);
+          v = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
+        }
+        *reinterpret_cast<float4*>(out + o) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e < N) {
+            float v = acc[i][j][e];
+            if (residual) v = residual[o + e] + v;
+            out[o + e] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MT, int NW>
+hipError_t launch_pp(const uint8_t* soa, const float* x, const float* residual, float* out,
+                     int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  const int64_t tm = (m + MT - 1) / MT;
+  const int64_t tn = (n + 4 * NW - 1) / (4 * NW);
+  if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(tm * tn));
+  hipLaunchKernelGGL((gemm_pp_kernel<MT, NW>), grid, dim3(512), 0, stream, soa,
+                     soa + scales_offset(n, k), x, residual, out, int(m), int(n), int(k), int(tm),
+                     int(tn));
+  return hipGetLastError();
+}
+
 template <int MT, int NW, int WN, int WK, int LIMBS>
 hipError_t launch_tile(const uint8_t* soa, const float* x, const float* residual, float* out,
                        int64_t m, int64_t n, int64_t k, hipStream_t stream) {
@@ -397,6 +714,8 @@ hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float
   if (m <= 32) return launch_tile<32, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
   if (m <= 64) return launch_tile<64, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
   if (m <= 128) return launch_tile<128, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
+  if (k <= int64_t(kPpMaxKB) * kBlockWeights)
+    return launch_pp<96, 48>(soa, x, residual, out, m, n, k, stream);
   return launch_tile<96, 48, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
 }
 
