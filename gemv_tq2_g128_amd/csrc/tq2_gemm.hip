@@ -93,8 +93,11 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Raw buffer resource over `bytes` bytes at `base`: loads past the end
-// return zero, loads take a 32-bit per-lane offset plus a scalar offset.
+// Raw buffer resource over `bytes` bytes at `base`: a load whose per-lane
+// offset (plus the instruction offset) reaches past the end returns zeros.
+// The hardware range check does not include the scalar offset operand, so
+// every variable offset here goes into the per-lane offset and the scalar
+// offset stays 0.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
                                            0x00020000);
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-          rx, aoff, i * AROWS * K * 4 + c * kChunk * 4, 0);
+          rx, aoff + uint32_t(i * AROWS * K * 4 + c * kChunk * 4), 0, 0);
       areg[i] = __builtin_bit_cast(float4, v);
     }
   };
@@ -191,16 +194,17 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
       if constexpr (QW == 4) {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, code_voff,
-                                                                j * 16 * (K / 4) + c * 64, 0);
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+            rc, code_voff + uint32_t(j * 16 * (K / 4) + c * 64), 0, 0);
         cw[j][0] = v[0]; cw[j][1] = v[1]; cw[j][2] = v[2]; cw[j][3] = v[3];
       } else {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, code_voff,
-                                                               j * 16 * (K / 4) + c * 64, 0);
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(
+            rc, code_voff + uint32_t(j * 16 * (K / 4) + c * 64), 0, 0);
         cw[j][0] = v[0]; cw[j][1] = v[1];
       }
       dsc[j] = __builtin_bit_cast(
-          _Float16, __builtin_amdgcn_raw_buffer_load_b16(rs, scale_voff, j * 16 * KB * 2 + c * 4, 0));
+          _Float16, __builtin_amdgcn_raw_buffer_load_b16(
+              rs, scale_voff + uint32_t(j * 16 * KB * 2 + c * 4), 0, 0));
     }
   };
 
@@ -445,11 +449,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   const int arow0 = grp * (MT / 2) + (gt >> 6);
   const uint32_t aoff = uint32_t(arow0) * uint32_t(K) * 4u + 16u * uint32_t(gt & 63);
   float4 areg[AV];
-  auto load_a = [&](int c) {
+  auto load_a = [&](int c, int lo, int hi) {
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
+      if (i < lo || i >= hi) continue;
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-          rx, aoff, i * AROWS * K * 4 + c * kChunk * 4, 0);
+          rx, aoff + uint32_t(i * AROWS * K * 4 + c * kChunk * 4), 0, 0);
       areg[i] = __builtin_bit_cast(float4, v);
     }
   };
@@ -469,8 +474,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   auto load_w = [&](int c) {
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, code_voff,
-                                                             j * 16 * (K / 4) + c * 64, 0);
+      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(
+            rc, code_voff + uint32_t(j * 16 * (K / 4) + c * 64), 0, 0);
       cw[j][0] = v[0];
       cw[j][1] = v[1];
     }
@@ -530,11 +535,15 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   };
   // MFMA phase: x fragments of step ss + 1 are read while step ss's MFMAs
   // issue (one LDS read per CG MFMAs), so every read has a step to land.
-  auto mfma_phase = [&](int c) {
+  // The MFMA phase also issues the second half of the x loads for chunk
+  // ca (the chunk this group stores in its next memory phase), spread over
+  // its first steps, so the memory phase issues fewer loads in one burst.
+  auto mfma_phase = [&](int c, int ca) {
     const int buf = c & 1;
     __builtin_amdgcn_s_setprio(1);
     half8_t a0[RT], a1[RT];
     load_afrags(buf, grp * STEPS, a0);
+    load_a(ca, AV / 2, AV);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ss = 0; ss < STEPS; ++ss) {
@@ -576,7 +585,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   auto mem_phase = [&](int cd, int cs, int cw_next) {
     decode_all(cd);
     store_a(cs & 1);
-    load_a(cs + 1);
+    load_a(cs + 1, 0, AV / 2);
     load_w(cw_next);
     pin_operands();
   };
@@ -600,10 +609,10 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
     const uint32_t o2 = full + 2u * uint32_t(tid);
     if (o2 < valid) Ls[o2 >> 1] = __builtin_amdgcn_raw_buffer_load_b16(rsb, o2, 0, 0);
   }
-  load_a(0);
+  load_a(0, 0, AV);
   load_w(0);
   store_a(0);
-  load_a(1);
+  load_a(1, 0, AV);
   lds_barrier();                         // scales visible
   if (grp == 0) {
     decode_all(0);
@@ -613,7 +622,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   lds_barrier();
   if (grp == 0) {
     for (int c = 0; c < nchunks; ++c) {
-      mfma_phase(c);
+      mfma_phase(c, c + 1);
       lds_barrier();
       mem_phase(c + 1, c + 1, c + 2);
       lds_barrier();
@@ -622,7 +631,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
     for (int c = 0; c < nchunks; ++c) {
       mem_phase(c, c + 1, c + 1);
       lds_barrier();
-      mfma_phase(c);
+      mfma_phase(c, c + 2);
       lds_barrier();
     }
   }
