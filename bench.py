@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-gemm", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-batched", action="store_true",
+                   help="skip the batched decode GEMV (16 weights per call)")
     p.add_argument("--no-chain", action="store_true",
                    help="skip the 100-layer M=1536 chain (config 5)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -249,6 +251,31 @@ def main():
                      "traffic_unit": "bytes per launch", "kernel": "gemv_kernel",
                      "us_per_launch": round(us_per_call, 3)},
     }
+
+    # ---- batched decode GEMV: 16 K = N = 4096 weights per call ----------------
+    if not args.no_batched:
+        nb = 16
+        calls = max(1, pool // nb)
+        outs = torch.empty((nb, n), dtype=torch.float32, device=dev)
+        ress = res.repeat(nb).reshape(nb, n)
+
+        def batched_call(i):
+            probs = [(base + ((i * nb + j) % pool) * sb, x.data_ptr(), ress[j].data_ptr(),
+                      outs[j].data_ptr(), n, k) for j in range(nb)]
+            st = tq2.gemv_batched_ptr(probs, torch.cuda.current_stream(dev).cuda_stream)
+            if st != 0:
+                raise RuntimeError("tq2_gemv_batched failed: %s" % tq2.status_string(st))
+
+        gb = capture(torch, stream, batched_call, calls)
+        time_graph(torch, gb, 2, stream)
+        reps = max(1, int(math.ceil(args.steps / (calls * nb))))
+        msb, _ = time_graph(torch, gb, reps, stream)
+        usb = msb * 1e3 / (reps * calls)
+        gbs_b = nb * nbytes / (usb * 1e-6) / 1e9
+        result["gemv_batched_16x4096x4096"] = {
+            "gbs": round(gbs_b, 2), "us_per_call": round(usb, 3), "weights_per_call": nb,
+            "bytes_per_call": nb * nbytes, "frac_of_hbm_peak": round(gbs_b / HBM_PEAK_GBS, 4),
+            "calls": reps * calls}
 
     # ---- large-M GEMM, M = 1536, K = N = 3072 --------------------------------
     if not args.no_gemm:

@@ -51,8 +51,9 @@ int check_shape(int64_t m, int64_t n, int64_t k) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? TQ2_OK : TQ2_ERR_LAUNCH; }
 
-// Checks common to tq2_gemv and tq2_gemm once the shape is valid and non-empty.
-int check_matmul_args(const void* soa, const float* x, const float* residual, const float* out,
+// Host-side checks common to the matmul entry points once the shape is valid
+// and non-empty: pointers, alignment and aliasing.
+int check_matmul_host(const void* soa, const float* x, const float* residual, const float* out,
                       int64_t m, int64_t n, int64_t k) {
   if (!soa || !x || !out) return TQ2_ERR_INVALID;
   if (!aligned(soa, 256) || !aligned(x, 16) || !aligned(out, 16) ||
@@ -62,7 +63,13 @@ int check_matmul_args(const void* soa, const float* x, const float* residual, co
   const size_t sb = tq2::soa_bytes(n, k);
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, soa, sb)) return TQ2_ERR_ALIAS;
   if (residual && residual != out && overlaps(out, ob, residual, ob)) return TQ2_ERR_ALIAS;
-  return check_device();
+  return TQ2_OK;
+}
+
+int check_matmul_args(const void* soa, const float* x, const float* residual, const float* out,
+                      int64_t m, int64_t n, int64_t k) {
+  const int st = check_matmul_host(soa, x, residual, out, m, n, k);
+  return st != TQ2_OK ? st : check_device();
 }
 
 }  // namespace
@@ -111,6 +118,61 @@ int tq2_gemv(const void* soa, const float* x, const float* residual, float* out,
   if (st != TQ2_OK) return st;
   return launch_status(tq2::launch_gemv(static_cast<const uint8_t*>(soa), x, residual, out, n,
                                         k, static_cast<hipStream_t>(stream)));
+}
+
+int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream) {
+  static_assert(TQ2_GEMV_BATCH_MAX == tq2::kGemvBatchMax, "batch limit");
+  if (count == 0) return TQ2_OK;
+  if (!problems || count < 0 || count > TQ2_GEMV_BATCH_MAX) return TQ2_ERR_INVALID;
+  for (int i = 0; i < count; ++i) {
+    const tq2_gemv_problem& p = problems[i];
+    int st = check_shape(1, p.n, p.k);
+    if (st != TQ2_OK) return st;
+    if (p.n == 0) continue;
+    st = check_matmul_host(p.soa, p.x, p.residual, p.out, 1, p.n, p.k);
+    if (st != TQ2_OK) return st;
+  }
+  // No problem's out may touch another problem's buffers.
+  for (int i = 0; i < count; ++i) {
+    const tq2_gemv_problem& p = problems[i];
+    if (p.n == 0) continue;
+    const size_t ob = size_t(p.n) * 4;
+    for (int j = 0; j < count; ++j) {
+      const tq2_gemv_problem& q = problems[j];
+      if (j == i || q.n == 0) continue;
+      if (overlaps(p.out, ob, q.out, size_t(q.n) * 4) ||
+          overlaps(p.out, ob, q.x, size_t(q.k) * 4) ||
+          overlaps(p.out, ob, q.soa, tq2::soa_bytes(q.n, q.k)) ||
+          overlaps(p.out, ob, q.residual, size_t(q.n) * 4))
+        return TQ2_ERR_ALIAS;
+    }
+  }
+  bool any = false;
+  for (int i = 0; i < count; ++i) any = any || problems[i].n > 0;
+  if (!any) return TQ2_OK;
+  const int dst = check_device();
+  if (dst != TQ2_OK) return dst;
+  // One launch per distinct k, in increasing k.
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t last_k = 0;
+  for (;;) {
+    int64_t k = 0;
+    for (int i = 0; i < count; ++i)
+      if (problems[i].n > 0 && problems[i].k > last_k && (k == 0 || problems[i].k < k))
+        k = problems[i].k;
+    if (k == 0) break;
+    tq2::GemvProblem group[tq2::kGemvBatchMax];
+    int ng = 0;
+    for (int i = 0; i < count; ++i) {
+      const tq2_gemv_problem& p = problems[i];
+      if (p.n > 0 && p.k == k)
+        group[ng++] = {static_cast<const uint8_t*>(p.soa), p.x, p.residual, p.out, p.n};
+    }
+    const int st = launch_status(tq2::launch_gemv_batched(group, ng, k, s));
+    if (st != TQ2_OK) return st;
+    last_k = k;
+  }
+  return TQ2_OK;
 }
 
 int tq2_gemm(const void* soa, const float* x, const float* residual, float* out, int64_t m,

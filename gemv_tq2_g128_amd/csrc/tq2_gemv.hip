@@ -110,15 +110,15 @@ __device__ __forceinline__ void accumulate_segment(const uint32_t (&cw)[ROWS],
   }
 }
 
-// ONE_SEG: K/16 <= LPS, the whole row fits one pass and every load of the
-// thread is issued before the first use.
+// One block's rows: block `blk` covers rows blk * OUTS .. blk * OUTS + OUTS - 1
+// of an [n_rows, k] weight.  ONE_SEG: K/16 <= LPS, the whole row fits one
+// pass and every load of the thread is issued before the first use.
 template <int ROWS, int LPS, bool ONE_SEG>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint32_t* __restrict__ codes,
-                                                        const uint16_t* __restrict__ scales,
-                                                        const float* __restrict__ x,
-                                                        const float* __restrict__ residual,
-                                                        float* __restrict__ out, int n_rows,
-                                                        int k) {
+__device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
+                                           const uint16_t* __restrict__ scales,
+                                           const float* __restrict__ x,
+                                           const float* __restrict__ residual,
+                                           float* __restrict__ out, int n_rows, int k, int blk) {
   constexpr int SLOTS = kThreads / LPS;
   constexpr int OUTS = SLOTS * ROWS;            // rows per block
   constexpr int G = kThreads / OUTS;            // threads that finish one row
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint32_t* __restri
   const int lw = SLOTS == 1 ? t : t % LPS;      // word index inside a K segment
   const int wpr = k >> 4;                       // code words per row
   const int kb_count = k >> 7;
-  const int row0 = blockIdx.x * OUTS + slot * ROWS;
+  const int row0 = blk * OUTS + slot * ROWS;
 
   float part[ROWS];
 #pragma unroll
@@ -174,12 +174,44 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint32_t* __restri
 #pragma unroll
   for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   if (g == 0) {
-    const int row = blockIdx.x * OUTS + os * ROWS + orr;
+    const int row = blk * OUTS + os * ROWS + orr;
     if (row < n_rows) {
       if (residual) v = residual[row] + v;
       out[row] = v;
     }
   }
+}
+
+template <int ROWS, int LPS, bool ONE_SEG>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint32_t* __restrict__ codes,
+                                                        const uint16_t* __restrict__ scales,
+                                                        const float* __restrict__ x,
+                                                        const float* __restrict__ residual,
+                                                        float* __restrict__ out, int n_rows,
+                                                        int k) {
+  gemv_block<ROWS, LPS, ONE_SEG>(codes, scales, x, residual, out, n_rows, k, blockIdx.x);
+}
+
+// Several independent GEMVs with the same k in one launch: block b belongs to
+// the problem p with first_block[p] <= b < first_block[p + 1].
+struct GemvBatchArgs {
+  const uint32_t* codes[kGemvBatchMax];
+  const uint16_t* scales[kGemvBatchMax];
+  const float* x[kGemvBatchMax];
+  const float* residual[kGemvBatchMax];
+  float* out[kGemvBatchMax];
+  int n[kGemvBatchMax];
+  int first_block[kGemvBatchMax + 1];
+  int count;
+};
+
+template <int ROWS, int LPS, bool ONE_SEG>
+__global__ __launch_bounds__(kThreads) void gemv_batched_kernel(const GemvBatchArgs args, int k) {
+  const int b = blockIdx.x;
+  int p = 0;
+  while (p + 1 < args.count && args.first_block[p + 1] <= b) ++p;   // uniform scan
+  gemv_block<ROWS, LPS, ONE_SEG>(args.codes[p], args.scales[p], args.x[p], args.residual[p],
+                                 args.out[p], args.n[p], k, b - args.first_block[p]);
 }
 
 template <int ROWS>
@@ -211,15 +243,79 @@ hipError_t launch_rows(int lps, const uint32_t* codes, const uint16_t* scales, c
   return hipGetLastError();
 }
 
+template <int ROWS>
+hipError_t launch_batched_rows(int lps, const GemvBatchArgs& args, int blocks, int k,
+                               hipStream_t stream) {
+  const dim3 grid(blocks);
+#define TQ2_GEMV_BCASE(L)                                                                    \
+  case L:                                                                                    \
+    hipLaunchKernelGGL((gemv_batched_kernel<ROWS, L, true>), grid, dim3(kThreads), 0, stream, \
+                       args, k);                                                             \
+    break;
+  switch (lps) {
+    TQ2_GEMV_BCASE(8)
+    TQ2_GEMV_BCASE(16)
+    TQ2_GEMV_BCASE(32)
+    TQ2_GEMV_BCASE(64)
+    TQ2_GEMV_BCASE(128)
+    default:
+      if (k / 16 <= 256)
+        hipLaunchKernelGGL((gemv_batched_kernel<ROWS, 256, true>), grid, dim3(kThreads), 0,
+                           stream, args, k);
+      else
+        hipLaunchKernelGGL((gemv_batched_kernel<ROWS, 256, false>), grid, dim3(kThreads), 0,
+                           stream, args, k);
+      break;
+  }
+#undef TQ2_GEMV_BCASE
+  return hipGetLastError();
+}
+
+// Lanes per row slot for a given k: a power of two >= k/16, at most 256.
+int lanes_per_slot(int64_t k) {
+  const int64_t wpr = k / 16;
+  int lps = 8;
+  while (lps < wpr && lps < kThreads) lps <<= 1;
+  return lps;
+}
+
 }  // namespace
+
+hipError_t launch_gemv_batched(const GemvProblem* probs, int count, int64_t k,
+                               hipStream_t stream) {
+  const int lps = lanes_per_slot(k);
+  const int slots = kThreads / lps;
+  int64_t rows_total = 0;
+  for (int p = 0; p < count; ++p) rows_total += probs[p].n;
+  // Rows per thread: 8 when that still gives >= 2 blocks per CU, else 4.
+  int rows = 8;
+  if ((rows_total + int64_t(slots) * 8 - 1) / (int64_t(slots) * 8) < 512) rows = 4;
+  if (rows > lps) rows = lps;
+  const int outs = slots * rows;
+  GemvBatchArgs args;
+  int64_t blocks = 0;
+  for (int p = 0; p < count; ++p) {
+    args.codes[p] = reinterpret_cast<const uint32_t*>(probs[p].soa);
+    args.scales[p] = reinterpret_cast<const uint16_t*>(probs[p].soa + scales_offset(probs[p].n, k));
+    args.x[p] = probs[p].x;
+    args.residual[p] = probs[p].residual;
+    args.out[p] = probs[p].out;
+    args.n[p] = int(probs[p].n);
+    args.first_block[p] = int(blocks);
+    blocks += (probs[p].n + outs - 1) / outs;
+  }
+  args.first_block[count] = int(blocks);
+  args.count = count;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (rows == 8) return launch_batched_rows<8>(lps, args, int(blocks), int(k), stream);
+  return launch_batched_rows<4>(lps, args, int(blocks), int(k), stream);
+}
 
 hipError_t launch_gemv(const uint8_t* soa, const float* x, const float* residual, float* out,
                        int64_t n, int64_t k, hipStream_t stream) {
   const uint32_t* codes = reinterpret_cast<const uint32_t*>(soa);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(soa + scales_offset(n, k));
-  const int64_t wpr = k / 16;
-  int lps = 8;
-  while (lps < wpr && lps < kThreads) lps <<= 1;
+  const int lps = lanes_per_slot(k);
   // Rows per thread: 8 when that still gives >= 2 blocks per CU, else fewer.
   const int slots = kThreads / lps;
   int rows = 8;

@@ -44,6 +44,18 @@ hipError_t launch_gemv(const uint8_t* soa, const float* x, const float* residual
 hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float* residual,
                        float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+// Batched decode GEMV: up to kGemvBatchMax independent problems with the same
+// k in one launch (their descriptors travel in the kernel arguments).
+constexpr int kGemvBatchMax = 32;
+struct GemvProblem {
+  const uint8_t* soa;
+  const float* x;
+  const float* residual;
+  float* out;
+  int64_t n;
+};
+hipError_t launch_gemv_batched(const GemvProblem* probs, int count, int64_t k, hipStream_t stream);
+
 // Largest M served by the split-f16 (f32-class) matrix-core path.
 constexpr int64_t kSplitMaxM = 16;
 

@@ -25,6 +25,8 @@ TQ2_ERR_ALIAS = -4
 TQ2_ERR_DEVICE = -5
 TQ2_ERR_LAUNCH = -6
 
+GEMV_BATCH_MAX = 32
+
 PATH_GEMV = 0
 PATH_SPLIT_F16 = 1
 PATH_F16 = 2
@@ -35,10 +37,17 @@ EXPORTED_SYMBOLS = (
     "tq2_soa_layout_version",
     "tq2_reformat_aos_to_soa",
     "tq2_gemv",
+    "tq2_gemv_batched",
     "tq2_gemm",
     "tq2_gemm_path",
     "tq2_status_string",
 )
+
+
+class GemvProblem(ctypes.Structure):
+    """Mirror of tq2_gemv_problem (include/tq2.h)."""
+    _fields_ = [("soa", ctypes.c_void_p), ("x", ctypes.c_void_p), ("residual", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64)]
 
 
 def _hip_runtimes_mapped():
@@ -79,6 +88,8 @@ def _load():
     lib.tq2_reformat_aos_to_soa.restype = c_int
     lib.tq2_gemv.argtypes = [vp, vp, vp, vp, i64, i64, vp]
     lib.tq2_gemv.restype = c_int
+    lib.tq2_gemv_batched.argtypes = [ctypes.POINTER(GemvProblem), c_int, vp]
+    lib.tq2_gemv_batched.restype = c_int
     lib.tq2_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.tq2_gemm.restype = c_int
     lib.tq2_gemm_path.argtypes = [i64, i64, i64]
@@ -137,6 +148,14 @@ def reformat_aos_to_soa_ptr(aos_ptr: int, soa_ptr: int, n: int, k: int, stream: 
 def gemv_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, n: int, k: int,
              stream: int = 0) -> int:
     return int(lib.tq2_gemv(soa_ptr, x_ptr, residual_ptr or None, out_ptr, n, k, stream or None))
+
+
+def gemv_batched_ptr(problems, stream: int = 0) -> int:
+    """problems: sequence of (soa_ptr, x_ptr, residual_ptr or 0, out_ptr, n, k)."""
+    arr = (GemvProblem * max(1, len(problems)))()
+    for i, (soa_p, x_p, r_p, o_p, n, k) in enumerate(problems):
+        arr[i] = GemvProblem(soa_p or None, x_p or None, r_p or None, o_p or None, n, k)
+    return int(lib.tq2_gemv_batched(arr, len(problems), stream or None))
 
 
 def gemm_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, n: int, k: int,
@@ -221,3 +240,29 @@ def gemm(soa, x, n: int, k: int, residual=None, out=None):
                     residual.data_ptr() if residual is not None else 0,
                     out.data_ptr(), m, n, k, _stream_handle(x.device)), "gemm")
     return out
+
+
+def gemv_batched(problems):
+    """Independent GEMVs in one call.  problems: sequence of dicts with keys
+    soa, x, n, k and optional residual, out.  Returns the list of outs."""
+    torch = _torch()
+    if len(problems) == 0:
+        return []
+    raw, outs, dev = [], [], None
+    for p in problems:
+        n, k = p["n"], p["k"]
+        _require(p["soa"], torch.uint8, soa_bytes(n, k), "soa")
+        _require(p["x"], torch.float32, k, "x")
+        res = p.get("residual")
+        if res is not None:
+            _require(res, torch.float32, n, "residual")
+        out = p.get("out")
+        if out is None:
+            out = torch.empty(n, dtype=torch.float32, device=p["x"].device)
+        _require(out, torch.float32, n, "out")
+        dev = p["x"].device
+        outs.append(out)
+        raw.append((p["soa"].data_ptr(), p["x"].data_ptr(), res.data_ptr() if res is not None else 0,
+                    out.data_ptr(), n, k))
+    _check(gemv_batched_ptr(raw, _stream_handle(dev)), "gemv_batched")
+    return outs

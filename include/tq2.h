@@ -89,6 +89,35 @@ int tq2_reformat_aos_to_soa(const void* aos, void* soa, int64_t n, int64_t k, vo
 int tq2_gemv(const void* soa, const float* x, const float* residual, float* out,
              int64_t n, int64_t k, void* stream);
 
+/* One independent decode GEMV of a batch (see tq2_gemv_batched). */
+typedef struct tq2_gemv_problem {
+  const void* soa;        /* tq2_soa_bytes(n, k) bytes from tq2_reformat_aos_to_soa */
+  const float* x;         /* f32 [k] */
+  const float* residual;  /* f32 [n] or NULL */
+  float* out;             /* f32 [n]; may equal residual */
+  int64_t n;
+  int64_t k;
+} tq2_gemv_problem;
+
+/* Most problems one tq2_gemv_batched call takes. */
+#define TQ2_GEMV_BATCH_MAX 32
+
+/* Several independent decode GEMVs, out_p = residual_p + W_p x_p, enqueued
+ * together: one launch per distinct k, all of that k's problems' row blocks
+ * in one grid, so the launch and ramp cost of a decode step with many
+ * projections is paid once rather than per weight (the decode path runs one
+ * TQ2 GEMV per projection: oxibonsai-kernels 0.1.5, pipelines.rs, field
+ * `gemv_tq2_g128_v1`).  Each problem follows tq2_gemv's rules and arithmetic;
+ * problems may share x, soa or residual buffers, but no problem's out may
+ * overlap any buffer of another problem.  `problems` is a HOST array of
+ * `count` entries, read during the call and not kept.  count == 0 and
+ * problems with n == 0 are no-ops.  Every problem is checked before anything
+ * is enqueued; a failed launch (TQ2_ERR_LAUNCH) may leave the launches for
+ * smaller k already enqueued.  Errors: INVALID (null problems with count > 0,
+ * count < 0 or count > TQ2_GEMV_BATCH_MAX, or a problem's argument), SHAPE,
+ * ALIGN, ALIAS, DEVICE, LAUNCH. */
+int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream);
+
 /* Batched matmul for any M >= 1: out[m, n] = residual[m, n] + sum_k x[m, k] w[n, k].
  * x: f32 [m, k] row-major; residual: f32 [m, n] or NULL; out: f32 [m, n],
  * same aliasing rules as tq2_gemv.  The kernel is picked by tq2_gemm_path:

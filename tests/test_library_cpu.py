@@ -23,7 +23,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     assert sorted(tq2.EXPORTED_SYMBOLS) == names
     lib = ctypes.CDLL(tq2.LIB_PATH)
     for name in names:
@@ -98,6 +98,27 @@ def test_argument_checks_before_any_device_work():
     assert r(0, 0, 0, 128) == tq2.TQ2_OK
 
 
+def test_batched_gemv_checks_before_any_device_work():
+    b = tq2.gemv_batched_ptr
+    X, O = A + 0x100000, A + 0x200000
+    ok = (A, X, 0, O, 8, 128)
+    assert b([]) == tq2.TQ2_OK
+    assert tq2.lib.tq2_gemv_batched(None, 1, None) == tq2.TQ2_ERR_INVALID
+    assert tq2.lib.tq2_gemv_batched(None, -1, None) == tq2.TQ2_ERR_INVALID
+    assert b([ok] * (tq2.GEMV_BATCH_MAX + 1)) == tq2.TQ2_ERR_INVALID
+    assert b([ok, (A, X, 0, O + 64, 8, 100)]) == tq2.TQ2_ERR_SHAPE
+    assert b([ok, (A, X, 0, 0, 8, 128)]) == tq2.TQ2_ERR_INVALID
+    assert b([ok, (A + 64, X, 0, O + 64, 8, 128)]) == tq2.TQ2_ERR_ALIGN
+    assert b([(A, X, 0, X, 8, 128)]) == tq2.TQ2_ERR_ALIAS           # out over its own x
+    # another problem's out over this problem's x, weight, out or residual
+    assert b([ok, (A + 0x10000, X + 0x1000, 0, X, 8, 128)]) == tq2.TQ2_ERR_ALIAS
+    assert b([ok, (A + 0x10000, X, 0, A + 16, 8, 128)]) == tq2.TQ2_ERR_ALIAS
+    assert b([ok, (A + 0x10000, X, 0, O + 16, 8, 128)]) == tq2.TQ2_ERR_ALIAS
+    assert b([(A, X, O + 0x100, O, 8, 128), (A, X, 0, O + 0x100, 8, 128)]) == tq2.TQ2_ERR_ALIAS
+    # empty problems are skipped; an all-empty batch is a no-op
+    assert b([(0, 0, 0, 0, 0, 128), (0, 0, 0, 0, 0, 256)]) == tq2.TQ2_OK
+
+
 def test_device_check_without_gpu():
     """Valid arguments but no gfx950 device: the call must return
     TQ2_ERR_DEVICE (never crash).  Only meaningful where no GPU is visible."""
@@ -105,4 +126,8 @@ def test_device_check_without_gpu():
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is visible; this check is for GPU-less hosts")
     st = tq2.gemm_ptr(A, A + 0x100000, 0, A + 0x200000, 4, 8, 128)
+    assert st == tq2.TQ2_ERR_DEVICE
+    # shared x and weight, distinct outs: valid, so the device check decides
+    st = tq2.gemv_batched_ptr([(A, A + 0x100000, 0, A + 0x200000, 8, 128),
+                               (A, A + 0x100000, 0, A + 0x200100, 8, 128)])
     assert st == tq2.TQ2_ERR_DEVICE

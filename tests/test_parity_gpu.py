@@ -263,3 +263,54 @@ def test_error_codes_with_device_pointers(tq2):
     assert p(0, x.data_ptr(), 0, out.data_ptr(), m, n, k) == tq2.TQ2_ERR_INVALID
     assert p(soa.data_ptr(), x.data_ptr(), res.data_ptr(), res.data_ptr(), m, n, k) == tq2.TQ2_OK
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Batched decode GEMV: independent problems in one call (one launch per k).
+# ---------------------------------------------------------------------------
+
+def _batched_check(tq2, specs, label):
+    """specs: list of (n, k, with_residual, x_from, inplace); x_from = index of
+    an earlier problem whose x this one shares, or None."""
+    cases, probs = [], []
+    for i, (n, k, with_res, x_from, inplace) in enumerate(specs):
+        c = G.random_case(5000 + 7 * i + n + k, 1, n, k, residual=with_res)
+        if x_from is not None:
+            c = dict(c, x=cases[x_from]["x"])
+        soa = upload_weight(tq2, c["aos"], n, k)
+        x = probs[x_from]["x"] if x_from is not None else _dev(c["x"].reshape(-1))
+        p = dict(soa=soa, x=x, n=n, k=k)
+        if with_res:
+            res = _dev(c["residual"].reshape(-1))
+            p["residual"] = res
+            if inplace:
+                p["out"] = res
+        cases.append(c)
+        probs.append(p)
+    print("batched case", label, [(c["n"], c["k"]) for c in cases], flush=True)
+    outs = tq2.gemv_batched(probs)
+    torch.cuda.synchronize()
+    for c, y in zip(cases, outs):
+        ref, s = oracle_full(c)
+        ok, msg = check(y.cpu().numpy().reshape(1, -1), ref, s, 0, "%s_n%d_k%d" % (label, c["n"], c["k"]))
+        print(msg, flush=True)
+        assert ok, msg
+
+
+def test_gemv_batched_mixed(tq2):
+    specs = [(300, 1024, False, None, False), (4096, 1024, True, None, False),
+             (77, 1024, False, 0, False), (1000, 4096, True, None, True), (9, 128, True, None, True),
+             (513, 4096, False, 3, False), (40, 20480, True, None, False)]
+    _batched_check(tq2, specs, "mixed")
+
+
+def test_gemv_batched_full_batch(tq2):
+    specs = [(64 + 5 * i, 128 * (1 + i % 3), i % 2 == 0, None, False)
+             for i in range(tq2.GEMV_BATCH_MAX)]
+    _batched_check(tq2, specs, "full")
+
+
+def test_gemv_batched_matches_oracle_at_decode_size(tq2):
+    specs = [(4096, 4096, True, None, False), (4096, 4096, True, 0, False),
+             (4096, 4096, False, 0, False)]
+    _batched_check(tq2, specs, "decode")
