@@ -275,7 +275,9 @@ def main():
         result["gemv_batched_16x4096x4096"] = {
             "gbs": round(gbs_b, 2), "us_per_call": round(usb, 3), "weights_per_call": nb,
             "bytes_per_call": nb * nbytes, "frac_of_hbm_peak": round(gbs_b / HBM_PEAK_GBS, 4),
-            "calls": reps * calls}
+            "calls": reps * calls,
+            "traffic": measured_traffic("gemv_batched_traffic_bytes_per_launch",
+                                        "gemv_tq2_g128_amd/csrc/tq2_gemv.hip")}
 
     # ---- large-M GEMM, M = 1536, K = N = 3072 --------------------------------
     if not args.no_gemm:
