@@ -300,6 +300,19 @@ def main():
         ms4, _ = time_graph(torch, g4, reps, stream)
         us4 = ms4 * 1e3 / (reps * per_graph)
         tflops = 2.0 * m4 * n4 * k4 / (us4 * 1e-6) / 1e12
+        def precise_call(i):
+            st = tq2.gemm_precise_ptr(soa4.data_ptr(), x4.data_ptr(), 0, out4.data_ptr(), m4, n4,
+                                      k4, torch.cuda.current_stream(dev).cuda_stream)
+            if st != 0:
+                raise RuntimeError("tq2_gemm_precise failed: %s" % tq2.status_string(st))
+
+        gp = capture(torch, stream, precise_call, per_graph)
+        time_graph(torch, gp, 1, stream)
+        msp, _ = time_graph(torch, gp, max(1, reps // 2), stream)
+        usp = msp * 1e3 / (max(1, reps // 2) * per_graph)
+        result["gemm_precise_m1536_k3072_n3072"] = {
+            "tflops": round(2.0 * m4 * n4 * k4 / (usp * 1e-6) / 1e12, 2),
+            "us_per_call": round(usp, 3), "path": 1, "tolerance": "1e-5 * sum|x w|"}
         result["gemm_m1536_k3072_n3072"] = {
             "tflops": round(tflops, 2), "us_per_call": round(us4, 3),
             "peak_tflops": F16_MFMA_PEAK_TFLOPS, "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),

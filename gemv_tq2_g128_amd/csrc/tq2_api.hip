@@ -193,6 +193,24 @@ int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
       tq2::launch_gemm(path, static_cast<const uint8_t*>(soa), x, residual, out, m, n, k, s));
 }
 
+int tq2_gemm_precise(const void* soa, const float* x, const float* residual, float* out,
+                     int64_t m, int64_t n, int64_t k, void* stream) {
+  int st = check_shape(m, n, k);
+  if (st != TQ2_OK) return st;
+  if (m == 0 || n == 0) return TQ2_OK;
+  st = check_matmul_args(soa, x, residual, out, m, n, k);
+  if (st != TQ2_OK) return st;
+  const int path = m <= 1 ? 0 : 1;
+  if (path != 0 && (k > tq2::kGemmMaxK || n * (k / 4) >= tq2::kGemmMaxCodeBytes))
+    return TQ2_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (path == 0)
+    return launch_status(
+        tq2::launch_gemv(static_cast<const uint8_t*>(soa), x, residual, out, n, k, s));
+  return launch_status(
+      tq2::launch_gemm(path, static_cast<const uint8_t*>(soa), x, residual, out, m, n, k, s));
+}
+
 const char* tq2_status_string(int status) {
   switch (status) {
     case TQ2_OK: return "ok";

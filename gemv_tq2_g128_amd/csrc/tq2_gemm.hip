@@ -719,7 +719,13 @@ hipError_t launch_tile(const uint8_t* soa, const float* x, const float* residual
 
 hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float* residual,
                        float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  if (path == 1) return launch_tile<16, 16, 4, 2, 2>(soa, x, residual, out, m, n, k, stream);
+  if (path == 1) {
+    // Split-binary16 (f32-class) kernel: 16-row tiles up to M = 16, 64-row
+    // tiles beyond (tq2_gemm_precise), so each weight is decoded once per 64
+    // rows of x.
+    if (m <= 16) return launch_tile<16, 16, 4, 2, 2>(soa, x, residual, out, m, n, k, stream);
+    return launch_tile<64, 16, 4, 2, 2>(soa, x, residual, out, m, n, k, stream);
+  }
   if (m <= 32) return launch_tile<32, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
   if (m <= 64) return launch_tile<64, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
   if (m <= 128) return launch_tile<128, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);

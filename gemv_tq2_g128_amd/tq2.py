@@ -39,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "tq2_gemv",
     "tq2_gemv_batched",
     "tq2_gemm",
+    "tq2_gemm_precise",
     "tq2_gemm_path",
     "tq2_status_string",
 )
@@ -92,6 +93,8 @@ def _load():
     lib.tq2_gemv_batched.restype = c_int
     lib.tq2_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.tq2_gemm.restype = c_int
+    lib.tq2_gemm_precise.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.tq2_gemm_precise.restype = c_int
     lib.tq2_gemm_path.argtypes = [i64, i64, i64]
     lib.tq2_gemm_path.restype = c_int
     lib.tq2_status_string.argtypes = [c_int]
@@ -164,6 +167,12 @@ def gemm_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, 
                             stream or None))
 
 
+def gemm_precise_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, n: int,
+                     k: int, stream: int = 0) -> int:
+    return int(lib.tq2_gemm_precise(soa_ptr, x_ptr, residual_ptr or None, out_ptr, m, n, k,
+                                    stream or None))
+
+
 # ---------------------------------------------------------------------------
 # torch.Tensor front end.
 # ---------------------------------------------------------------------------
@@ -223,8 +232,9 @@ def gemv(soa, x, n: int, k: int, residual=None, out=None):
     return out
 
 
-def gemm(soa, x, n: int, k: int, residual=None, out=None):
-    """out[m, n] = residual[m, n] + sum_k x[m, k] * w[n, k]; x is f32 [m, k]."""
+def gemm(soa, x, n: int, k: int, residual=None, out=None, precise: bool = False):
+    """out[m, n] = residual[m, n] + sum_k x[m, k] * w[n, k]; x is f32 [m, k].
+    precise=True calls tq2_gemm_precise (f32-class accuracy at every M)."""
     torch = _torch()
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x must be [m, %d]" % k)
@@ -236,9 +246,10 @@ def gemm(soa, x, n: int, k: int, residual=None, out=None):
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _require(out, torch.float32, m * n, "out")
-    _check(gemm_ptr(soa.data_ptr(), x.data_ptr(),
-                    residual.data_ptr() if residual is not None else 0,
-                    out.data_ptr(), m, n, k, _stream_handle(x.device)), "gemm")
+    call = gemm_precise_ptr if precise else gemm_ptr
+    _check(call(soa.data_ptr(), x.data_ptr(), residual.data_ptr() if residual is not None else 0,
+                out.data_ptr(), m, n, k, _stream_handle(x.device)),
+           "gemm_precise" if precise else "gemm")
     return out
 
 

@@ -134,6 +134,18 @@ int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream);
 int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
              int64_t m, int64_t n, int64_t k, void* stream);
 
+/* tq2_gemm with f32-class accuracy at every M: the split-binary16 matrix-core
+ * kernel of path 1 (x = hi + lo, both parts against the same exact binary16
+ * weight, f32 accumulation) for every M >= 2, and the GEMV for M == 1; error
+ * within 1e-5 * sum|x w| for |x| <= 65504, at about twice path 2's matrix-core
+ * work for M > 16.  The pages stage both operands as binary16 for large M
+ * (pipelines.rs, fields `gemm_tq2_g128_v9_simdgroup` /
+ * `gemm_tq2_g128_v10_simdgroup`); this is the variant for callers that need
+ * the f32 path's accuracy (their `gemm_tq2_g128_v7` / `_v8_tiled`).  Same
+ * arguments, rules and errors as tq2_gemm. */
+int tq2_gemm_precise(const void* soa, const float* x, const float* residual, float* out,
+                     int64_t m, int64_t n, int64_t k, void* stream);
+
 /* The kernel tq2_gemm uses for this shape (0, 1 or 2 as listed above), or
  * TQ2_ERR_INVALID / TQ2_ERR_SHAPE for an invalid shape.  Pure host function. */
 int tq2_gemm_path(int64_t m, int64_t n, int64_t k);

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     assert sorted(tq2.EXPORTED_SYMBOLS) == names
     lib = ctypes.CDLL(tq2.LIB_PATH)
     for name in names:
@@ -92,6 +92,11 @@ def test_argument_checks_before_any_device_work():
     assert r(A, A, 8, 128) == tq2.TQ2_ERR_ALIAS
     assert r(0, A, 8, 128) == tq2.TQ2_ERR_INVALID
     # empty shapes are no-ops that touch nothing, even with null pointers
+    pg = tq2.gemm_precise_ptr
+    assert pg(A, A + 0x100000, 0, A + 0x200000, 4, 8, 100) == tq2.TQ2_ERR_SHAPE
+    assert pg(A + 64, A + 0x100000, 0, A + 0x200000, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert pg(A, A + 0x100000, 0, A + 0x100000, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert pg(0, 0, 0, 0, 0, 8, 128) == tq2.TQ2_OK
     assert g(0, 0, 0, 0, 0, 8, 128) == tq2.TQ2_OK
     assert g(0, 0, 0, 0, 4, 0, 128) == tq2.TQ2_OK
     assert v(0, 0, 0, 0, 0, 128) == tq2.TQ2_OK

@@ -32,7 +32,7 @@ def upload_weight(tq2, aos, n, k):
     return tq2.reformat_aos_to_soa(_dev(aos), n, k)
 
 
-def run_case(tq2, case, force_gemv=False, inplace=False):
+def run_case(tq2, case, force_gemv=False, inplace=False, precise=False):
     m, n, k = case["m"], case["n"], case["k"]
     soa = upload_weight(tq2, case["aos"], n, k)
     x = _dev(case["x"].reshape(m, k))
@@ -44,7 +44,7 @@ def run_case(tq2, case, force_gemv=False, inplace=False):
         y = tq2.gemv(soa, x.reshape(-1), n, k, residual=None if res_arg is None else res_arg.reshape(-1),
                      out=None if out is None else out.reshape(-1))
     else:
-        y = tq2.gemm(soa, x, n, k, residual=res_arg, out=out)
+        y = tq2.gemm(soa, x, n, k, residual=res_arg, out=out, precise=precise)
     torch.cuda.synchronize()
     return y.cpu().numpy().reshape(m, n)
 
@@ -59,7 +59,12 @@ def assert_case(tq2, case, **kw):
     print("case", case["name"], kw, flush=True)
     got = run_case(tq2, case, **kw)
     ref, s = oracle_full(case)
-    path = 0 if kw.get("force_gemv") else tq2.gemm_path(case["m"], case["n"], case["k"])
+    if kw.get("force_gemv") or case["m"] == 1:
+        path = 0
+    elif kw.get("precise"):
+        path = 1
+    else:
+        path = tq2.gemm_path(case["m"], case["n"], case["k"])
     ok, msg = check(got, ref, s, path, case["name"])
     print(msg, flush=True)
     assert ok, msg
@@ -314,3 +319,22 @@ def test_gemv_batched_matches_oracle_at_decode_size(tq2):
     specs = [(4096, 4096, True, None, False), (4096, 4096, True, 0, False),
              (4096, 4096, False, 0, False)]
     _batched_check(tq2, specs, "decode")
+
+
+# ---------------------------------------------------------------------------
+# tq2_gemm_precise: f32-class accuracy (1e-5 * S) at every M.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,n,k", [(1, 300, 1024), (2, 77, 384), (17, 200, 384), (64, 129, 1024),
+                                   (65, 300, 640), (100, 1000, 4096), (129, 191, 384)])
+def test_gemm_precise_shapes(tq2, m, n, k):
+    c = G.random_case(3000 + m + n + k, m, n, k, residual=True)
+    assert_case(tq2, c, precise=True)
+
+
+def test_gemm_precise_config3_m100(tq2):
+    assert_case(tq2, dict(G.config3(100), name="config3_m100_precise"), precise=True)
+
+
+def test_gemm_precise_config4(tq2):
+    assert_case(tq2, dict(G.config4(), name="config4_precise"), precise=True)
