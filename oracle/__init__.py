@@ -13,11 +13,16 @@ from .tq2_oracle import (  # noqa: F401
     dequantize,
     dequantize_block_scalar,
     dequantize_scalar,
+    SILU_SLOPE_BOUND,
     error_scale,
     f16_bits_to_float,
     f16_bits_to_float_array,
+    gate_up_swiglu,
+    gate_up_swiglu_entries,
+    gate_up_swiglu_error_scale,
     matmul,
     matmul_entries,
     matmul_rows,
     matmul_scalar,
+    silu,
 )

@@ -33,8 +33,21 @@ Everything is evaluated in float64.  ``dequantize`` and the sums are written
 out plainly; the large-size path uses NumPy's float64 matrix product as the
 summation step, which the tests pin against the scalar triple loop.
 
+Fused gate/up projections with SwiGLU (the ternary counterpart of the
+``fused_gate_up_swiglu_q1`` / ``fused_gate_up_swiglu_gemm_q1`` pipelines of
+oxibonsai-kernels 0.1.5, pipelines.rs, ``MetalPipelines``, decode and prefill
+sections; their arithmetic is not printed, and the element-wise ``silu_f32``
+pipeline of the same table names the activation)::
+
+    out[m, n] = silu(g[m, n]) * u[m, n],   silu(z) = z / (1 + exp(-z)),
+    g = x @ W_gate^T,  u = x @ W_up^T      (two [N, K] ternary weights)
+
+read as the usual SwiGLU feed-forward gate: SiLU of the gate projection times
+the up projection, element by element, with no residual.
+
 Parity pins: the f16 decoder, block size, code map, bit order and the
-contraction are pinned by ``tests/test_oracle.py``.  The bit order and the
+contraction are pinned by ``tests/test_oracle.py``, and so are SiLU and the
+gate/up composition.  The bit order and the
 code map are the recorded convention above -- the pages print neither -- so
 they are pinned to that convention, not to a worked example of the pages.
 """
@@ -235,3 +248,54 @@ def matmul_rows(aos: np.ndarray, x: np.ndarray, n: int, k: int, cols, residual=N
         ref = r + ref
         s = s + np.abs(r)
     return ref, s
+
+
+# ---------------------------------------------------------------------------
+# Fused gate/up projections + SwiGLU.
+# ---------------------------------------------------------------------------
+
+# Upper bound of |d silu / dz| over the reals: silu'(z) = s (1 + z (1 - s)) with
+# s = 1 / (1 + exp(-z)) peaks at about 1.0998 near z = 2.4.
+SILU_SLOPE_BOUND = 1.1
+
+
+def silu(z):
+    """SiLU ``z / (1 + exp(-z))`` in float64 (0 for z -> -inf, z for z -> +inf)."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def gate_up_swiglu(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray, n: int,
+                   k: int) -> np.ndarray:
+    """float64 ``silu(x @ W_gate^T) * (x @ W_up^T)``, shape ``[M, n]``."""
+    g = matmul(aos_gate, x, n, k)
+    u = matmul(aos_up, x, n, k)
+    return silu(g) * u
+
+
+def _swiglu_scale(g, u, sg, su, tol):
+    # |silu(g + dg) (u + du) - silu(g) u|
+    #     <= |silu(g + dg) - silu(g)| |u + du| + |silu(g)| |du|
+    #     <= tol * (SLOPE * sg * (|u| + tol * su) + |silu(g)| * su)
+    # for |dg| <= tol * sg and |du| <= tol * su.
+    return SILU_SLOPE_BOUND * sg * (np.abs(u) + tol * su) + np.abs(silu(g)) * su
+
+
+def gate_up_swiglu_error_scale(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray,
+                               n: int, k: int, tol: float) -> np.ndarray:
+    """Scale ``E`` such that projections each within ``tol * sum_k |x w|`` of
+    the exact values give an output within ``tol * E`` of the exact one."""
+    g = matmul(aos_gate, x, n, k)
+    u = matmul(aos_up, x, n, k)
+    sg = error_scale(aos_gate, x, n, k)
+    su = error_scale(aos_up, x, n, k)
+    return _swiglu_scale(g, u, sg, su, tol)
+
+
+def gate_up_swiglu_entries(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray, n: int,
+                           k: int, rows, cols, tol: float):
+    """Reference and error scale ``E`` for selected outputs ``(rows[i], cols[i])``."""
+    g, sg = matmul_entries(aos_gate, x, n, k, rows, cols)
+    u, su = matmul_entries(aos_up, x, n, k, rows, cols)
+    return silu(g) * u, _swiglu_scale(g, u, sg, su, tol)

@@ -403,3 +403,150 @@ def test_pins_catch_planted_sum_mistakes(kind):
     results = [pin_two_block_row(mm), pin_closed_forms(mm), pin_symmetries(mm),
                pin_against_scalar_triple_loop(mm)]
     assert not all(results), kind
+
+
+# ---------------------------------------------------------------------------
+# SiLU and the fused gate/up + SwiGLU composition (the ternary counterpart of
+# the fused_gate_up_swiglu_q1 / fused_gate_up_swiglu_gemm_q1 pipelines of
+# oxibonsai-kernels 0.1.5, pipelines.rs).  SiLU(z) = z * logistic(z); the pins
+# use the logistic function's textbook values, SciPy's expit as an
+# independent library route, and the identity silu(z) - silu(-z) = z.
+# ---------------------------------------------------------------------------
+
+from scipy.special import expit  # noqa: E402
+
+LOGISTIC_1 = 0.7310585786300049      # 1 / (1 + e^-1)
+LOGISTIC_2 = 0.8807970779778823      # 1 / (1 + e^-2)
+
+
+def pin_silu_values(silu):
+    z = np.linspace(-30.0, 30.0, 6001)
+    ok = float(silu(0.0)) == 0.0
+    ok &= abs(float(silu(1.0)) - LOGISTIC_1) <= 2e-16
+    ok &= abs(float(silu(-1.0)) - (LOGISTIC_1 - 1.0)) <= 2e-16
+    ok &= abs(float(silu(2.0)) - 2.0 * LOGISTIC_2) <= 4e-16
+    ok &= np.allclose(silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
+    ok &= np.allclose(silu(z) - silu(-z), z, rtol=0, atol=1e-13)
+    big = silu(np.array([800.0, -800.0]))
+    ok &= bool(np.all(np.isfinite(big))) and big[0] == 800.0 and big[1] == 0.0
+    # the slope bound used by the error scale holds and is nearly tight
+    zz = np.linspace(-20.0, 20.0, 400001)
+    slope = np.diff(silu(zz)) / np.diff(zz)
+    ok &= slope.max() < O.SILU_SLOPE_BOUND and slope.max() > 1.09 and slope.min() > -0.11
+    return bool(ok)
+
+
+def pin_swiglu_hand_worked(sw):
+    # One row x = 1 (K = 128).  Gate: every code 2 (+1), d = 2^-6 -> g = 2.
+    # Up: every code 0 (-1), d = 0.5 -> u = -64.  out = silu(2) * (-64)
+    # = -128 * logistic(2).
+    gate = np.frombuffer(block([0xAA] * 32, 0x2400), np.uint8)
+    up = np.frombuffer(block([0x00] * 32, 0x3800), np.uint8)
+    x = np.ones((1, 128), np.float32)
+    return abs(float(sw(gate, up, x, 1, 128)[0, 0]) + 128.0 * LOGISTIC_2) <= 1e-12
+
+
+def pin_swiglu_structure(sw):
+    n, k = 6, 384
+    c = G.swiglu_case(41, 3, n, k)
+    gate, up, x = c["gate"], c["up"], c["x"]
+    base = sw(gate, up, x, n, k)
+    ok = True
+    # a zero gate or a zero up projection gives zero
+    ok &= np.array_equal(sw(_replace_codes(gate, n, k, 0x55), up, x, n, k), np.zeros((3, n)))
+    ok &= np.array_equal(sw(gate, _replace_codes(up, n, k, 0x55), x, n, k), np.zeros((3, n)))
+    # negating the up weight negates the output; negating the gate does not
+    neg = _swap02_table()
+    ok &= np.allclose(sw(gate, _replace_codes(up, n, k, byte_map=neg), x, n, k), -base,
+                      rtol=1e-13, atol=1e-15)
+    ok &= not np.allclose(sw(_replace_codes(gate, n, k, byte_map=neg), up, x, n, k), -base,
+                          rtol=1e-6, atol=1e-9)
+    # gate == up: out = u^2 logistic(u) >= 0
+    ok &= bool(np.all(sw(up, up, x, n, k) >= 0))
+    # a row permutation applied to both weights permutes the output columns
+    perm = np.array([4, 0, 5, 1, 3, 2])
+    gp = gate.reshape(n, -1)[perm].reshape(-1)
+    upp = up.reshape(n, -1)[perm].reshape(-1)
+    ok &= np.array_equal(sw(gp, upp, x, n, k), base[:, perm])
+    # against the scalar triple loop and SciPy's logistic function
+    gs = np.array(O.matmul_scalar(bytes(gate), x.tolist(), n, k))
+    us = np.array(O.matmul_scalar(bytes(up), x.tolist(), n, k))
+    ok &= np.allclose(base, gs * expit(gs) * us, rtol=1e-12, atol=1e-15)
+    return bool(ok)
+
+
+def test_silu_values():
+    assert pin_silu_values(O.silu)
+
+
+def test_swiglu_hand_worked():
+    assert pin_swiglu_hand_worked(O.gate_up_swiglu)
+
+
+def test_swiglu_structure():
+    assert pin_swiglu_structure(O.gate_up_swiglu)
+
+
+def test_swiglu_error_scale_bounds_perturbations():
+    # Projections moved by up to tol * sum_k |x w| (every sign pattern, plus
+    # random points inside the box) move the output by at most tol * E.
+    n, k = 8, 512
+    c = G.swiglu_case(42, 4, n, k, probs=G.UNIFORM_TERNARY, d_range=(0.05, 0.5))
+    gate, up, x = c["gate"], c["up"], c["x"]
+    g, u = O.matmul(gate, x, n, k), O.matmul(up, x, n, k)
+    sg, su = O.error_scale(gate, x, n, k), O.error_scale(up, x, n, k)
+    ref = O.gate_up_swiglu(gate, up, x, n, k)
+    rng = np.random.default_rng(7)
+    for tol in (1e-5, 2e-3, 0.05):
+        e = O.gate_up_swiglu_error_scale(gate, up, x, n, k, tol)
+        trials = [(a, b) for a in (-1.0, 1.0) for b in (-1.0, 1.0)]
+        trials += [tuple(rng.uniform(-1, 1, size=(2,) + g.shape)) for _ in range(20)]
+        for a, b in trials:
+            moved = O.silu(g + a * tol * sg) * (u + b * tol * su)
+            assert np.all(np.abs(moved - ref) <= tol * e * (1 + 1e-12) + 1e-300)
+    # and it is not loose by orders of magnitude where the gate is steep
+    e = O.gate_up_swiglu_error_scale(gate, up, x, n, k, 2e-3)
+    moved = O.silu(g + 2e-3 * sg) * u
+    assert np.max(np.abs(moved - ref) / (2e-3 * e)) > 0.2
+
+
+def test_swiglu_entries_match_full():
+    n, k = 9, 256
+    c = G.swiglu_case(43, 5, n, k)
+    full = O.gate_up_swiglu(c["gate"], c["up"], c["x"], n, k)
+    e_full = O.gate_up_swiglu_error_scale(c["gate"], c["up"], c["x"], n, k, 1e-5)
+    rows, cols = np.array([0, 4, 2]), np.array([8, 0, 3])
+    ref, e = O.gate_up_swiglu_entries(c["gate"], c["up"], c["x"], n, k, rows, cols, 1e-5)
+    assert np.allclose(ref, full[rows, cols], rtol=1e-13, atol=1e-15)
+    assert np.allclose(e, e_full[rows, cols], rtol=1e-13)
+
+
+def _mutant_swiglu(kind):
+    def silu(z):
+        z = np.asarray(z, np.float64)
+        if kind == "sigmoid":
+            return expit(z)
+        if kind == "exp_sign":
+            return z / (1.0 + np.exp(np.minimum(z, 700)))
+        if kind == "relu":
+            return np.maximum(z, 0.0)
+        return O.silu(z)
+
+    def sw(gate, up, x, n, k):
+        g = O.matmul(gate, x, n, k)
+        u = O.matmul(up, x, n, k)
+        if kind == "swapped":
+            g, u = u, g
+        if kind == "sum":
+            return silu(g) + u
+        if kind == "gate_only":
+            return silu(g)
+        return silu(g) * u
+    return silu, sw
+
+
+@pytest.mark.parametrize("kind", ["sigmoid", "exp_sign", "relu", "swapped", "sum", "gate_only"])
+def test_pins_catch_planted_swiglu_mistakes(kind):
+    silu, sw = _mutant_swiglu(kind)
+    results = [pin_silu_values(silu), pin_swiglu_hand_worked(sw), pin_swiglu_structure(sw)]
+    assert not all(results), kind

@@ -172,3 +172,31 @@ def random_case(seed: int, m: int, n: int, k: int, probs=UNIFORM_TERNARY,
     x = make_activations(rng, m, k, outlier_frac=outlier_frac)
     r = rng.standard_normal((m, n), dtype=np.float32) if residual else None
     return dict(name=f"case_s{seed}_m{m}_n{n}_k{k}", m=m, n=n, k=k, aos=w, x=x, residual=r)
+
+
+def swiglu_case(seed: int, m: int, n: int, k: int, probs=HALF_ZERO_TERNARY,
+                d_range=(0.005, 0.05), outlier_frac: float = 0.0):
+    """Gate and up weights (both ``[n, k]``) and activations ``[m, k]`` for the
+    fused gate/up + SwiGLU op; defaults follow the prefill GEMM workload's
+    code and scale distributions."""
+    rng = np.random.default_rng(seed)
+    gate = make_weight(rng, n, k, probs, d_range)
+    up = make_weight(rng, n, k, probs, d_range)
+    x = make_activations(rng, m, k, outlier_frac=outlier_frac)
+    return dict(name=f"swiglu_s{seed}_m{m}_n{n}_k{k}", m=m, n=n, k=k, gate=gate, up=up, x=x)
+
+
+# Feed-forward gate/up workload: K = 4096 -> N = 11008 (the prefill GEMM
+# workload's projection shape), half-zero codes, d ~ U[0.005, 0.05].
+SWIGLU_K, SWIGLU_N = 4096, 11008
+SWIGLU_WEIGHT_SEED = 33
+
+
+def swiglu_workload(m: int):
+    """Gate/up weights of the feed-forward workload and ``m`` activation rows."""
+    rng = np.random.default_rng(SWIGLU_WEIGHT_SEED)
+    gate = make_weight(rng, SWIGLU_N, SWIGLU_K, HALF_ZERO_TERNARY, (0.005, 0.05))
+    up = make_weight(rng, SWIGLU_N, SWIGLU_K, HALF_ZERO_TERNARY, (0.005, 0.05))
+    x = make_activations(np.random.default_rng(SWIGLU_WEIGHT_SEED + 1 + m), m, SWIGLU_K)
+    return dict(name=f"swiglu_m{m}_k{SWIGLU_K}_n{SWIGLU_N}", m=m, n=SWIGLU_N, k=SWIGLU_K,
+                gate=gate, up=up, x=x)
