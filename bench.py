@@ -40,6 +40,8 @@ def parse():
                    help="skip the batched decode GEMV (16 weights per call)")
     p.add_argument("--no-chain", action="store_true",
                    help="skip the 100-layer M=1536 chain (config 5)")
+    p.add_argument("--no-swiglu", action="store_true",
+                   help="skip the fused gate/up + SwiGLU lines (K=4096 -> N=11008)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device-to-device copy of this size (MiB) so a "
                         "counter run can scale FETCH_SIZE / WRITE_SIZE against known bytes")
@@ -177,6 +179,67 @@ def chain_bench(torch, tq2, G, dev, stream):
             "gemm_tflops": round(flop / (kernels_ms * 1e-3) / 1e12, 2),
             "gemm_frac": round(flop / (kernels_ms * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS, 4),
             "with_glue_ms": round(chain_ms, 4)}
+
+
+def swiglu_bench(torch, tq2, G, dev, stream, args):
+    """Fused gate/up + SwiGLU, K = 4096 -> N = 11008 (half-zero codes):
+    decode (M = 1, gate/up pairs rotated over copies larger than the Infinity
+    Cache, as for the GEMV) in GB/s of algorithmic bytes, and prefill
+    (M = 1536) in TFLOP/s (4 M N K flop per call: two projections)."""
+    n, k = G.SWIGLU_N, G.SWIGLU_K
+    gate, up = G.swiglu_weights()
+    gs = tq2.reformat_aos_to_soa(torch.from_numpy(gate).to(dev), n, k)
+    us = tq2.reformat_aos_to_soa(torch.from_numpy(up).to(dev), n, k)
+    sb = tq2.soa_bytes(n, k)
+    pool = max(1, int(math.ceil(args.pool_mib * 2 ** 20 / (2 * sb))))
+    gpool, upool = gs.repeat(pool), us.repeat(pool)
+    gb, ub = gpool.data_ptr(), upool.data_ptr()
+    x1 = torch.from_numpy(G.swiglu_activations(1)).to(dev)
+    out1 = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+    def decode_call(i):
+        st = tq2.gate_up_swiglu_ptr(gb + (i % pool) * sb, ub + (i % pool) * sb, x1.data_ptr(),
+                                    out1.data_ptr(), 1, n, k,
+                                    torch.cuda.current_stream(dev).cuda_stream)
+        if st != 0:
+            raise RuntimeError("tq2_gate_up_swiglu failed: %s" % tq2.status_string(st))
+
+    g1 = capture(torch, stream, decode_call, pool)
+    time_graph(torch, g1, 2, stream)
+    reps = max(1, int(math.ceil(args.steps / 4 / pool)))
+    ms1, _ = time_graph(torch, g1, reps, stream)
+    us1 = ms1 * 1e3 / (reps * pool)
+    nbytes = 2 * n * (k // 128) * 34 + 4 * k + 4 * n
+    gbs = nbytes / (us1 * 1e-6) / 1e9
+    del g1, gpool, upool
+
+    m = 1536
+    xm = torch.from_numpy(G.swiglu_activations(m)).to(dev)
+    outm = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+    def prefill_call(i):
+        st = tq2.gate_up_swiglu_ptr(gs.data_ptr(), us.data_ptr(), xm.data_ptr(), outm.data_ptr(),
+                                    m, n, k, torch.cuda.current_stream(dev).cuda_stream)
+        if st != 0:
+            raise RuntimeError("tq2_gate_up_swiglu failed: %s" % tq2.status_string(st))
+
+    per_graph = 10
+    gm = capture(torch, stream, prefill_call, per_graph)
+    time_graph(torch, gm, 1, stream)
+    repm = max(1, args.gemm_reps // 40)
+    msm, _ = time_graph(torch, gm, repm, stream)
+    usm = msm * 1e3 / (repm * per_graph)
+    tflops = 4.0 * m * n * k / (usm * 1e-6) / 1e12
+    return {
+        "swiglu_decode_k4096_n11008": {
+            "gbs": round(gbs, 2), "us_per_call": round(us1, 3), "bytes_per_call": nbytes,
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "calls": reps * pool,
+            "pairs_rotated": pool},
+        "swiglu_prefill_m1536_k4096_n11008": {
+            "tflops": round(tflops, 2), "us_per_call": round(usm, 3),
+            "peak_tflops": F16_MFMA_PEAK_TFLOPS, "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
+            "path": tq2.gemm_path(m, n, k), "calls": repm * per_graph},
+    }
 
 
 def main():
@@ -319,6 +382,9 @@ def main():
             "path": tq2.gemm_path(m4, n4, k4), "calls": reps * per_graph,
             "traffic": measured_traffic("gemm_traffic_bytes_per_launch",
                                         "gemv_tq2_g128_amd/csrc/tq2_gemm.hip")}
+
+    if not args.no_swiglu:
+        result.update(swiglu_bench(torch, tq2, G, dev, stream, args))
 
     if not args.no_chain:
         result["chain_100_layers_m1536"] = chain_bench(torch, tq2, G, dev, stream)

@@ -211,6 +211,29 @@ int tq2_gemm_precise(const void* soa, const float* x, const float* residual, flo
       tq2::launch_gemm(path, static_cast<const uint8_t*>(soa), x, residual, out, m, n, k, s));
 }
 
+int tq2_gate_up_swiglu(const void* gate_soa, const void* up_soa, const float* x, float* out,
+                       int64_t m, int64_t n, int64_t k, void* stream) {
+  int st = check_shape(m, n, k);
+  if (st != TQ2_OK) return st;
+  if (m == 0 || n == 0) return TQ2_OK;
+  if (!up_soa) return TQ2_ERR_INVALID;
+  st = check_matmul_host(gate_soa, x, nullptr, out, m, n, k);
+  if (st != TQ2_OK) return st;
+  if (!aligned(up_soa, 256)) return TQ2_ERR_ALIGN;
+  if (overlaps(out, size_t(m) * size_t(n) * 4, up_soa, tq2::soa_bytes(n, k)))
+    return TQ2_ERR_ALIAS;
+  const int path = tq2_gemm_path(m, n, k);
+  if (path != 0 && (k > tq2::kGemmMaxK || n * (k / 4) >= tq2::kGemmMaxCodeBytes))
+    return TQ2_ERR_INVALID;
+  st = check_device();
+  if (st != TQ2_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* g = static_cast<const uint8_t*>(gate_soa);
+  const uint8_t* u = static_cast<const uint8_t*>(up_soa);
+  if (path == 0) return launch_status(tq2::launch_gemv_swiglu(g, u, x, out, n, k, s));
+  return launch_status(tq2::launch_gemm_swiglu(path, g, u, x, out, m, n, k, s));
+}
+
 const char* tq2_status_string(int status) {
   switch (status) {
     case TQ2_OK: return "ok";

@@ -22,6 +22,11 @@
 //    the same exact weight operand: f32-class accuracy (about 2^-22).
 //  * gemm_pp_kernel (large M) runs its two wave groups half a chunk apart:
 //    one group issues MFMAs while the other decodes, converts and loads.
+//  * SWIGLU (the ternary counterpart of `fused_gate_up_swiglu_gemm_q1` in the
+//    same table): half of the block's waves take gate-weight columns and the
+//    other half the same columns of the up weight, on the same x tile; the
+//    epilogue meets each pair in LDS and stores silu(g) * u, silu(z) =
+//    z / (1 + e^-z).  Neither projection goes to memory.
 //  * Blocks are numbered so that the N-tiles of the same M rows land on the
 //    same XCD (the dispatcher deals block ids round-robin over 8 XCDs): x, at
 //    4 bytes per element, is the costly operand to re-fetch, so an XCD's L2
@@ -89,6 +94,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -105,23 +112,26 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 // Block tile MT x (WN*NW); WN waves split the columns, WK waves split each
 // 256-wide chunk's eight MFMA steps (their partial sums meet in LDS at the
-// end).  Each wave owns MT rows x NW columns of the tile.
-template <int MT, int NW, int WN, int WK, int LIMBS>
-__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __restrict__ codes,
-                                                            const uint8_t* __restrict__ scales,
-                                                            const float* __restrict__ x,
-                                                            const float* __restrict__ residual,
-                                                            float* __restrict__ out, int M, int N,
-                                                            int K, int tiles_m, int tiles_n) {
+// end).  Each wave owns MT rows x NW columns of the tile.  With SWIGLU the
+// waves wn < WN/2 read the gate weight (codes, scales) and the others the
+// same columns of the up weight (ucodes, uscales): the output tile is
+// MT x (WN/2 * NW).
+template <int MT, int NW, int WN, int WK, int LIMBS, bool SWIGLU>
+__global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
+    const float* __restrict__ x, const float* __restrict__ residual, float* __restrict__ out,
+    int M, int N, int K, int tiles_m, int tiles_n) {
   constexpr int THREADS = 64 * WN * WK;
   constexpr int RT = MT / 16;            // 16-row MFMA tiles per wave
   constexpr int CG = NW / 16;            // 16-column groups per wave
-  constexpr int NT = WN * NW;
+  constexpr int NT = SWIGLU ? WN / 2 * NW : WN * NW;   // output columns per block
   constexpr int STEPS = 8 / WK;          // MFMA k-steps per wave per chunk
   constexpr int QW = 4 / WK;             // code dwords per lane per chunk
   constexpr int AV = MT * (kChunk / 4) / THREADS;   // float4 A loads per thread per chunk
   static_assert(MT % 16 == 0 && NW % 16 == 0, "tile shape");
   static_assert(WK == 1 || WK == 2, "k split");
+  static_assert(!SWIGLU || WN % 2 == 0, "gate/up wave split");
   static_assert((MT * (kChunk / 4)) % THREADS == 0, "A staging split");
 
   __shared__ _Float16 As[2][LIMBS][MT][kLdsRow];
@@ -140,6 +150,9 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   const int wave = tid >> 6;
   const int wn = wave % WN;              // column share
   const int wk = wave / WN;              // share of the chunk's steps
+  // Gate or up weight (wave-uniform), and the column share inside it.
+  const bool upw = SWIGLU && __builtin_amdgcn_readfirstlane(wn) >= WN / 2;
+  const int wc = SWIGLU ? wn % (WN / 2) : wn;
   const int lane = tid & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
@@ -149,8 +162,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
 
   // x rows m0 .. m0+MT-1 (rows past M read as zero).
   const rsrc_t rx = make_rsrc(x + size_t(m0) * K, uint32_t(min(MT, M - m0)) * uint32_t(K) * 4u);
-  const rsrc_t rc = make_rsrc(codes, uint32_t(N) * uint32_t(K / 4));
-  const rsrc_t rs = make_rsrc(scales, uint32_t(N) * uint32_t(KB) * 2u);
+  const rsrc_t rc = make_rsrc(upw ? ucodes : codes, uint32_t(N) * uint32_t(K / 4));
+  const rsrc_t rs = make_rsrc(upw ? uscales : scales, uint32_t(N) * uint32_t(KB) * 2u);
 
   // Per-thread byte offsets, fixed for the whole K loop; a chunk, an A row
   // step and a column group add scalar offsets.  Columns past N read as zero
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
   // QW code dwords of its column and k-group that this wave's steps use, and
   // the raw binary16 scale of the block they fall in.  Columns past N read as
   // zero codes and zero scales.
-  const uint32_t nl = uint32_t(n0 + wn * NW + col);
+  const uint32_t nl = uint32_t(n0 + wc * NW + col);
   const uint32_t code_voff = nl * uint32_t(K / 4) + 16u * uint32_t(g) + 4u * QW * uint32_t(wk);
   const uint32_t scale_voff = (nl * uint32_t(KB) + uint32_t(g >> 1)) * 2u;
   auto load_w = [&](int c, codes_t (&cw)[CG], _Float16 (&dsc)[CG]) {
@@ -336,14 +349,44 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
             red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
     }
     __syncthreads();
-    if (wk == 1) return;
+    if constexpr (!SWIGLU) {
+      if (wk == 1) return;
+    }
+    if (wk == 0) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j][e] += red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane];
+    }
+  }
+
+  // ---- SwiGLU: each up wave hands its sums to the gate wave of its columns -
+  if constexpr (SWIGLU) {
+    float* red = reinterpret_cast<float*>(&As[0][0][0][0]);
+    static_assert(WN * RT * CG * 4 * 64 * 4 <= sizeof(As), "exchange buffer");
+    // An up wave overwrites only the slots its own lanes have just read.
+    if (wk == 0 && upw) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (wk != 0 || upw) return;
+    const int wu = wn + WN / 2;
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int j = 0; j < CG; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[i][j][e] += red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane];
+          acc[i][j][e] = silu(acc[i][j][e]) * red[(((wu * RT + i) * CG + j) * 4 + e) * 64 + lane];
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -358,7 +401,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
     if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const int n = n0 + wn * NW + j * 16 + 4 * g;
+      const int n = n0 + wc * NW + j * 16 + 4 * g;
       const size_t o = size_t(m) * N + n;
       if (vec && n + 3 < N) {
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
@@ -398,17 +441,20 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(const uint8_t* __res
 // MFMA(c), group 0 MEM.  x tile c + 1 is stored in two halves, by group 1 in
 // phase A and by group 0 in phase B, into the buffer nobody reads during
 // chunk c.
-template <int MT, int NW>
-__global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict__ codes,
-                                                      const uint8_t* __restrict__ scales,
-                                                      const float* __restrict__ x,
-                                                      const float* __restrict__ residual,
-                                                      float* __restrict__ out, int M, int N, int K,
-                                                      int tiles_m, int tiles_n) {
+//
+// SWIGLU: waves wn = 0, 1 of each group read gate-weight columns, waves 2, 3
+// the same columns of the up weight; the output tile is MT x 2NW.
+template <int MT, int NW, bool SWIGLU>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
+    const float* __restrict__ x, const float* __restrict__ residual, float* __restrict__ out,
+    int M, int N, int K, int tiles_m, int tiles_n) {
   constexpr int GT = 256;                // threads per group
   constexpr int RT = MT / 16;
   constexpr int CG = NW / 16;
-  constexpr int NT = 4 * NW;
+  constexpr int NT = 4 * NW;             // weight rows per block
+  constexpr int NO = SWIGLU ? 2 * NW : NT;   // output columns per block
   constexpr int STEPS = 4;               // MFMA steps per group per chunk
   constexpr int QW = 2;                  // code dwords per lane per chunk
   constexpr int AV = MT * (kChunk / 4) / 2 / GT;   // float4 of x per thread per chunk
@@ -417,7 +463,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
 
   __shared__ _Float16 As[2][MT][kLdsRow];
   // The block's scales for the whole K (NT rows of the scales plane, which
-  // are contiguous), loaded once.
+  // are contiguous; with SWIGLU 2NW gate rows, then the same 2NW up rows),
+  // loaded once.
   __shared__ __attribute__((aligned(16))) uint16_t Ls[NT * kPpMaxKB];
 
   const int ntiles = tiles_m * tiles_n;
@@ -426,12 +473,15 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   const int mt = t / tiles_n;
   const int nt = t - mt * tiles_n;
   const int m0 = mt * MT;
-  const int n0 = nt * NT;
+  const int n0 = nt * NO;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int grp = wave >> 2;
   const int wn = wave & 3;
+  // Gate or up weight (wave-uniform), and the column share inside it.
+  const bool upw = SWIGLU && __builtin_amdgcn_readfirstlane(wn) >= 2;
+  const int wc = SWIGLU ? (wn & 1) : wn;
   const int lane = tid & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
@@ -440,8 +490,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   const int nchunks = (K + kChunk - 1) / kChunk;
 
   const rsrc_t rx = make_rsrc(x + size_t(m0) * K, uint32_t(min(MT, M - m0)) * uint32_t(K) * 4u);
-  const rsrc_t rc = make_rsrc(codes, uint32_t(N) * uint32_t(K / 4));
-  const rsrc_t rs = make_rsrc(scales, uint32_t(N) * uint32_t(KB) * 2u);
+  const rsrc_t rc = make_rsrc(upw ? ucodes : codes, uint32_t(N) * uint32_t(K / 4));
 
   // x staging: group p converts rows p*MT/2 .. p*MT/2 + MT/2 - 1 of a chunk;
   // its thread gt handles float4 f = gt + GT*i: row f / 64, float4 f % 64.
@@ -468,7 +517,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   };
 
   // Weights: lane's column, its k-group g, this group's half of the steps.
-  const uint32_t nl = uint32_t(n0 + wn * NW + col);
+  const uint32_t nl = uint32_t(n0 + wc * NW + col);
   const uint32_t code_voff = nl * uint32_t(K / 4) + 16u * uint32_t(g) + 4u * QW * uint32_t(grp);
   uint32_t cw[CG][QW];
   auto load_w = [&](int c) {
@@ -599,15 +648,27 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
     // of a buffer resource returns zeros in full), 2-byte loads for the tail.
     // Entries for columns past N are left unset: their outputs are never
     // stored.
-    const uint32_t valid = uint32_t(min(NT, N - n0)) * uint32_t(KB) * 2u;
-    const uint32_t full = valid & ~15u;
-    const rsrc_t rsb = make_rsrc(scales + size_t(n0) * KB * 2, valid);
-    for (uint32_t o = 16u * uint32_t(tid); o < full; o += 16u * 512u) {
-      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsb, o, 0, 0);
-      *reinterpret_cast<u32x4_t*>(reinterpret_cast<uint8_t*>(Ls) + o) = v;
+    auto preload = [&](const uint8_t* plane, int rows, int dst) {
+      const uint32_t valid = uint32_t(min(rows, N - n0)) * uint32_t(KB) * 2u;
+      const uint32_t full = valid & ~15u;
+      const rsrc_t rsb = make_rsrc(plane + size_t(n0) * KB * 2, valid);
+      uint8_t* ls = reinterpret_cast<uint8_t*>(Ls + dst);
+      for (uint32_t o = 16u * uint32_t(tid); o < full; o += 16u * 512u) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsb, o, 0, 0);
+        *reinterpret_cast<u32x4_t*>(ls + o) = v;
+      }
+      const uint32_t o2 = full + 2u * uint32_t(tid);
+      if (o2 < valid)
+        *reinterpret_cast<uint16_t*>(ls + o2) = __builtin_amdgcn_raw_buffer_load_b16(rsb, o2, 0, 0);
+    };
+    if constexpr (SWIGLU) {
+      // Gate rows at Ls row 0, up rows at Ls row 2NW: 2NW * KB * 2 bytes is a
+      // multiple of 16 (NW is a multiple of 16), so both halves stay aligned.
+      preload(scales, 2 * NW, 0);
+      preload(uscales, 2 * NW, 2 * NW * KB);
+    } else {
+      preload(scales, NT, 0);
     }
-    const uint32_t o2 = full + 2u * uint32_t(tid);
-    if (o2 < valid) Ls[o2 >> 1] = __builtin_amdgcn_raw_buffer_load_b16(rsb, o2, 0, 0);
   }
   load_a(0, 0, AV);
   load_w(0);
@@ -649,14 +710,41 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
           red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
   }
   __syncthreads();
-  if (grp == 1) return;
+  if constexpr (!SWIGLU) {
+    if (grp == 1) return;
+  }
+  if (grp == 0) {
 #pragma unroll
-  for (int i = 0; i < RT; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < CG; ++j)
+      for (int j = 0; j < CG; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        acc[i][j][e] += red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane];
+        for (int e = 0; e < 4; ++e)
+          acc[i][j][e] += red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane];
+  }
+  if constexpr (SWIGLU) {
+    // Group 0's up waves hand their sums to the gate waves of their columns
+    // (each overwrites only the slots its own lanes have just read).
+    if (grp == 0 && upw) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (grp == 1 || upw) return;
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CG; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[i][j][e] =
+              silu(acc[i][j][e]) * red[((((wn + 2) * RT + i) * CG + j) * 4 + e) * 64 + lane];
+  }
 
   const bool vec = (N & 3) == 0;
 #pragma unroll
@@ -665,7 +753,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
     if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const int n = n0 + wn * NW + j * 16 + 4 * g;
+      const int n = n0 + wc * NW + j * 16 + 4 * g;
       const size_t o = size_t(m) * N + n;
       if (vec && n + 3 < N) {
         float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
@@ -688,50 +776,74 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const uint8_t* __restrict_
   }
 }
 
-template <int MT, int NW>
-hipError_t launch_pp(const uint8_t* soa, const float* x, const float* residual, float* out,
-                     int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+// `up` is null for the plain matmul; with SWIGLU, `soa` is the gate weight.
+template <int MT, int NW, bool SWIGLU>
+hipError_t launch_pp(const uint8_t* soa, const uint8_t* up, const float* x,
+                     const float* residual, float* out, int64_t m, int64_t n, int64_t k,
+                     hipStream_t stream) {
+  constexpr int NO = SWIGLU ? 2 * NW : 4 * NW;
   const int64_t tm = (m + MT - 1) / MT;
-  const int64_t tn = (n + 4 * NW - 1) / (4 * NW);
+  const int64_t tn = (n + NO - 1) / NO;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(unsigned(tm * tn));
-  hipLaunchKernelGGL((gemm_pp_kernel<MT, NW>), grid, dim3(512), 0, stream, soa,
-                     soa + scales_offset(n, k), x, residual, out, int(m), int(n), int(k), int(tm),
+  const size_t so = scales_offset(n, k);
+  hipLaunchKernelGGL((gemm_pp_kernel<MT, NW, SWIGLU>), grid, dim3(512), 0, stream, soa, soa + so,
+                     up, up ? up + so : nullptr, x, residual, out, int(m), int(n), int(k), int(tm),
                      int(tn));
   return hipGetLastError();
 }
 
-template <int MT, int NW, int WN, int WK, int LIMBS>
-hipError_t launch_tile(const uint8_t* soa, const float* x, const float* residual, float* out,
-                       int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+template <int MT, int NW, int WN, int WK, int LIMBS, bool SWIGLU>
+hipError_t launch_tile(const uint8_t* soa, const uint8_t* up, const float* x,
+                       const float* residual, float* out, int64_t m, int64_t n, int64_t k,
+                       hipStream_t stream) {
+  constexpr int NO = SWIGLU ? WN / 2 * NW : WN * NW;
   const int64_t tm = (m + MT - 1) / MT;
-  const int64_t tn = (n + WN * NW - 1) / (WN * NW);
+  const int64_t tn = (n + NO - 1) / NO;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = int(tm), tiles_n = int(tn);
   const dim3 grid(unsigned(tm * tn));
-  hipLaunchKernelGGL((gemm_kernel<MT, NW, WN, WK, LIMBS>), grid, dim3(64 * WN * WK), 0, stream,
-                     soa, soa + scales_offset(n, k), x, residual, out, int(m), int(n), int(k),
-                     tiles_m, tiles_n);
+  const size_t so = scales_offset(n, k);
+  hipLaunchKernelGGL((gemm_kernel<MT, NW, WN, WK, LIMBS, SWIGLU>), grid, dim3(64 * WN * WK), 0,
+                     stream, soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m),
+                     int(n), int(k), tiles_m, tiles_n);
   return hipGetLastError();
+}
+
+// Kernel choice by path and M (shared by the plain and the SwiGLU forms).
+template <bool SWIGLU>
+hipError_t dispatch(int path, const uint8_t* soa, const uint8_t* up, const float* x,
+                    const float* residual, float* out, int64_t m, int64_t n, int64_t k,
+                    hipStream_t stream) {
+  if (path == 1) {
+    // Split-binary16 (f32-class) kernel: 16-row tiles up to M = 16, 64-row
+    // tiles beyond (tq2_gemm_precise), so each weight is decoded once per 64
+    // rows of x.
+    if (m <= 16)
+      return launch_tile<16, 16, 4, 2, 2, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+    return launch_tile<64, 16, 4, 2, 2, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+  }
+  if (m <= 32)
+    return launch_tile<32, 16, 4, 2, 1, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+  if (m <= 64)
+    return launch_tile<64, 16, 4, 2, 1, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+  if (m <= 128)
+    return launch_tile<128, 16, 4, 2, 1, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+  if (k <= int64_t(kPpMaxKB) * kBlockWeights)
+    return launch_pp<96, 48, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+  return launch_tile<96, 48, 4, 2, 1, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float* residual,
                        float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  if (path == 1) {
-    // Split-binary16 (f32-class) kernel: 16-row tiles up to M = 16, 64-row
-    // tiles beyond (tq2_gemm_precise), so each weight is decoded once per 64
-    // rows of x.
-    if (m <= 16) return launch_tile<16, 16, 4, 2, 2>(soa, x, residual, out, m, n, k, stream);
-    return launch_tile<64, 16, 4, 2, 2>(soa, x, residual, out, m, n, k, stream);
-  }
-  if (m <= 32) return launch_tile<32, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
-  if (m <= 64) return launch_tile<64, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
-  if (m <= 128) return launch_tile<128, 16, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
-  if (k <= int64_t(kPpMaxKB) * kBlockWeights)
-    return launch_pp<96, 48>(soa, x, residual, out, m, n, k, stream);
-  return launch_tile<96, 48, 4, 2, 1>(soa, x, residual, out, m, n, k, stream);
+  return dispatch<false>(path, soa, nullptr, x, residual, out, m, n, k, stream);
+}
+
+hipError_t launch_gemm_swiglu(int path, const uint8_t* gate, const uint8_t* up, const float* x,
+                              float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  return dispatch<true>(path, gate, up, x, nullptr, out, m, n, k, stream);
 }
 
 }  // namespace tq2

@@ -214,6 +214,98 @@ __global__ __launch_bounds__(kThreads) void gemv_batched_kernel(const GemvBatchA
                                  args.out[p], args.n[p], k, b - args.first_block[p]);
 }
 
+// Fused gate/up projections + SwiGLU, decode (M = 1):
+//     out[n] = silu(g[n]) * u[n],  g = W_gate x,  u = W_up x,
+// silu(z) = z / (1 + e^-z) (oxibonsai-kernels 0.1.5, pipelines.rs,
+// `MetalPipelines`: `fused_gate_up_swiglu_q1`, here for ternary weights).
+// Lane t owns one code word of 8 rows, as in gemv_block: rows 0..3 of its
+// slot's gate weight and the same 4 rows of the up weight, so a block streams
+// both weights' rows for its outputs and the finishing thread of output n
+// holds g[n] and u[n] together.  Neither projection leaves the chip.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+template <int LPS, bool ONE_SEG>
+__global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
+    const uint32_t* __restrict__ gcodes, const uint16_t* __restrict__ gscales,
+    const uint32_t* __restrict__ ucodes, const uint16_t* __restrict__ uscales,
+    const float* __restrict__ x, float* __restrict__ out, int n_rows, int k) {
+  constexpr int HALF = 4;                       // outputs per slot
+  constexpr int ROWS = 2 * HALF;                // weight rows per lane
+  constexpr int SLOTS = kThreads / LPS;
+  constexpr int OUTS = SLOTS * HALF;            // outputs per block
+  constexpr int G = kThreads / OUTS;            // threads that finish one output
+  static_assert(LPS >= ROWS && G >= 1 && G <= 64, "reduction shape");
+  const int t = threadIdx.x;
+  const int slot = SLOTS == 1 ? 0 : t / LPS;
+  const int lw = SLOTS == 1 ? t : t % LPS;
+  const int wpr = k >> 4;
+  const int kb_count = k >> 7;
+  const int out0 = blockIdx.x * OUTS + slot * HALF;
+
+  float part[ROWS];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) part[r] = 0.f;
+  uint32_t cw[ROWS];
+  uint32_t db[ROWS];
+  float xv[16];
+  // Rows 0..HALF-1 from the gate weight, HALF..ROWS-1 from the up weight.
+  auto load = [&](int wc) {
+    const unsigned uwc = unsigned(wc);
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int row = min(out0 + (r % HALF), n_rows - 1);
+      const uint32_t* crow = (r < HALF ? gcodes : ucodes) + size_t(row) * wpr;
+      const uint16_t* srow = (r < HALF ? gscales : uscales) + size_t(row) * kb_count;
+      cw[r] = crow[uwc];
+      db[r] = srow[uwc >> 3];
+    }
+    const float4* xp = reinterpret_cast<const float4*>(x + 16 * wc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 q = xp[i];
+      xv[4 * i] = q.x;
+      xv[4 * i + 1] = q.y;
+      xv[4 * i + 2] = q.z;
+      xv[4 * i + 3] = q.w;
+    }
+  };
+  if constexpr (ONE_SEG) {
+    const bool live = lw < wpr;
+    load(live ? lw : wpr - 1);
+    accumulate_segment<ROWS>(cw, db, xv, live, part);
+  } else {
+    for (int seg = 0; seg < wpr; seg += LPS) {
+      const int w = seg + lw;
+      const bool live = w < wpr;
+      load(live ? w : wpr - 1);
+      accumulate_segment<ROWS>(cw, db, xv, live, part);
+    }
+  }
+
+  __shared__ float red[ROWS][kThreads];
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) red[r][t] = part[r];
+  __syncthreads();
+  const int o = t / G;                          // block output finished by this thread
+  const int os = o / HALF;
+  const int orr = o % HALF;
+  const int g = t % G;
+  constexpr int PER = LPS / G;
+  float vg = 0.f, vu = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    vg += red[orr][os * LPS + g * PER + i];
+    vu += red[orr + HALF][os * LPS + g * PER + i];
+  }
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) {
+    vg += __shfl_xor(vg, off, 64);
+    vu += __shfl_xor(vu, off, 64);
+  }
+  const int row = blockIdx.x * OUTS + o;
+  if (g == 0 && row < n_rows) out[row] = silu(vg) * vu;
+}
+
 template <int ROWS>
 hipError_t launch_rows(int lps, const uint32_t* codes, const uint16_t* scales, const float* x,
                        const float* residual, float* out, int n, int k, hipStream_t stream) {
@@ -280,6 +372,42 @@ int lanes_per_slot(int64_t k) {
 }
 
 }  // namespace
+
+hipError_t launch_gemv_swiglu(const uint8_t* gate, const uint8_t* up, const float* x,
+                              float* out, int64_t n, int64_t k, hipStream_t stream) {
+  const uint32_t* gc = reinterpret_cast<const uint32_t*>(gate);
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(gate + scales_offset(n, k));
+  const uint32_t* uc = reinterpret_cast<const uint32_t*>(up);
+  const uint16_t* us = reinterpret_cast<const uint16_t*>(up + scales_offset(n, k));
+  const int lps = lanes_per_slot(k);
+  const int outs = (kThreads / lps) * 4;
+  const int64_t blocks = (n + outs - 1) / outs;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const int ni = int(n), ki = int(k);
+#define TQ2_SWIGLU_CASE(L)                                                                    \
+  case L:                                                                                     \
+    hipLaunchKernelGGL((gemv_swiglu_kernel<L, true>), grid, dim3(kThreads), 0, stream, gc, gs, \
+                       uc, us, x, out, ni, ki);                                               \
+    break;
+  switch (lps) {
+    TQ2_SWIGLU_CASE(8)
+    TQ2_SWIGLU_CASE(16)
+    TQ2_SWIGLU_CASE(32)
+    TQ2_SWIGLU_CASE(64)
+    TQ2_SWIGLU_CASE(128)
+    default:
+      if (k / 16 <= 256)
+        hipLaunchKernelGGL((gemv_swiglu_kernel<256, true>), grid, dim3(kThreads), 0, stream, gc,
+                           gs, uc, us, x, out, ni, ki);
+      else
+        hipLaunchKernelGGL((gemv_swiglu_kernel<256, false>), grid, dim3(kThreads), 0, stream, gc,
+                           gs, uc, us, x, out, ni, ki);
+      break;
+  }
+#undef TQ2_SWIGLU_CASE
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv_batched(const GemvProblem* probs, int count, int64_t k,
                                hipStream_t stream) {

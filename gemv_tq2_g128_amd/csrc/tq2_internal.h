@@ -44,6 +44,14 @@ hipError_t launch_gemv(const uint8_t* soa, const float* x, const float* residual
 hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float* residual,
                        float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+// Fused gate/up projections + SwiGLU: out = silu(x W_gate^T) * (x W_up^T),
+// both weights [n, k] in SoA v1.  The GEMV form serves M = 1; the matrix-core
+// form takes `path` 1 or 2 as launch_gemm does.
+hipError_t launch_gemv_swiglu(const uint8_t* gate, const uint8_t* up, const float* x,
+                              float* out, int64_t n, int64_t k, hipStream_t stream);
+hipError_t launch_gemm_swiglu(int path, const uint8_t* gate, const uint8_t* up, const float* x,
+                              float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream);
+
 // Batched decode GEMV: up to kGemvBatchMax independent problems with the same
 // k in one launch (their descriptors travel in the kernel arguments).
 constexpr int kGemvBatchMax = 32;

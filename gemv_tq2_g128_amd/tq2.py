@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "tq2_gemv_batched",
     "tq2_gemm",
     "tq2_gemm_precise",
+    "tq2_gate_up_swiglu",
     "tq2_gemm_path",
     "tq2_status_string",
 )
@@ -95,6 +96,8 @@ def _load():
     lib.tq2_gemm.restype = c_int
     lib.tq2_gemm_precise.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.tq2_gemm_precise.restype = c_int
+    lib.tq2_gate_up_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.tq2_gate_up_swiglu.restype = c_int
     lib.tq2_gemm_path.argtypes = [i64, i64, i64]
     lib.tq2_gemm_path.restype = c_int
     lib.tq2_status_string.argtypes = [c_int]
@@ -171,6 +174,12 @@ def gemm_precise_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, 
                      k: int, stream: int = 0) -> int:
     return int(lib.tq2_gemm_precise(soa_ptr, x_ptr, residual_ptr or None, out_ptr, m, n, k,
                                     stream or None))
+
+
+def gate_up_swiglu_ptr(gate_ptr: int, up_ptr: int, x_ptr: int, out_ptr: int, m: int, n: int,
+                       k: int, stream: int = 0) -> int:
+    return int(lib.tq2_gate_up_swiglu(gate_ptr or None, up_ptr or None, x_ptr or None,
+                                      out_ptr or None, m, n, k, stream or None))
 
 
 # ---------------------------------------------------------------------------
@@ -277,3 +286,21 @@ def gemv_batched(problems):
                     out.data_ptr(), n, k))
     _check(gemv_batched_ptr(raw, _stream_handle(dev)), "gemv_batched")
     return outs
+
+
+def gate_up_swiglu(gate_soa, up_soa, x, n: int, k: int, out=None):
+    """out[m, n] = silu(x W_gate^T)[m, n] * (x W_up^T)[m, n]; x is f32 [m, k]."""
+    torch = _torch()
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be [m, %d]" % k)
+    m = x.shape[0]
+    _require(gate_soa, torch.uint8, soa_bytes(n, k), "gate_soa")
+    _require(up_soa, torch.uint8, soa_bytes(n, k), "up_soa")
+    _require(x, torch.float32, m * k, "x")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _require(out, torch.float32, m * n, "out")
+    _check(gate_up_swiglu_ptr(gate_soa.data_ptr(), up_soa.data_ptr(), x.data_ptr(),
+                              out.data_ptr(), m, n, k, _stream_handle(x.device)),
+           "gate_up_swiglu")
+    return out

@@ -146,6 +146,30 @@ int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
 int tq2_gemm_precise(const void* soa, const float* x, const float* residual, float* out,
                      int64_t m, int64_t n, int64_t k, void* stream);
 
+/* Fused gate/up projections with SwiGLU, for any M >= 1:
+ *     out[m, n] = silu(g[m, n]) * u[m, n],  silu(z) = z / (1 + exp(-z)),
+ *     g = x W_gate^T,  u = x W_up^T.
+ * The ternary counterpart of the pages' `fused_gate_up_swiglu_q1` (decode)
+ * and `fused_gate_up_swiglu_gemm_q1` (prefill) pipelines (oxibonsai-kernels
+ * 0.1.5, pipelines.rs, `MetalPipelines`); the pages name the fusion, and the
+ * arithmetic is the usual SwiGLU gate with SiLU as in their `silu_f32`.
+ * gate_soa, up_soa: two [n, k] weights in this library's SoA layout (256-byte
+ * aligned device buffers from tq2_reformat_aos_to_soa; they may be the same
+ * buffer).  x: f32 [m, k] row-major; out: f32 [m, n] row-major, which must not
+ * overlap x or either weight.  Both projections stay on chip: each output
+ * tile reads x once for both weights.  The kernels follow tq2_gemm_path:
+ * M == 1 runs a fused f32 GEMV, 2 <= M <= 16 the split-binary16 matrix-core
+ * kernel, M > 16 the binary16 matrix-core kernel, with g and u each as
+ * accurate as tq2_gemm's result on that path (tolerance tol = 1e-5 or
+ * 2e-3 of sum|x w|); out is then within
+ *     tol * (1.1 * Sg * (|u| + tol * Su) + |silu(g)| * Su)
+ * plus a few f32 roundings of |out|, where Sg, Su are sum_k |x w| of each
+ * projection (1.1 bounds silu's slope).  m == 0 or n == 0 is a no-op.
+ * Errors: INVALID (null pointer or oversized shape), SHAPE, ALIGN, ALIAS,
+ * DEVICE, LAUNCH. */
+int tq2_gate_up_swiglu(const void* gate_soa, const void* up_soa, const float* x, float* out,
+                       int64_t m, int64_t n, int64_t k, void* stream);
+
 /* The kernel tq2_gemm uses for this shape (0, 1 or 2 as listed above), or
  * TQ2_ERR_INVALID / TQ2_ERR_SHAPE for an invalid shape.  Pure host function. */
 int tq2_gemm_path(int64_t m, int64_t n, int64_t k);

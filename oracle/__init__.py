@@ -20,9 +20,11 @@ from .tq2_oracle import (  # noqa: F401
     gate_up_swiglu,
     gate_up_swiglu_entries,
     gate_up_swiglu_error_scale,
+    gate_up_swiglu_parts,
     matmul,
     matmul_entries,
     matmul_rows,
     matmul_scalar,
     silu,
+    swiglu_from_parts,
 )

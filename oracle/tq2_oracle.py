@@ -293,6 +293,25 @@ def gate_up_swiglu_error_scale(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.n
     return _swiglu_scale(g, u, sg, su, tol)
 
 
+def gate_up_swiglu_parts(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray, n: int,
+                         k: int):
+    """``(g, u, Sg, Su)``: both projections and their ``sum_k |x w|`` scales,
+    each weight decoded once (for large cases)."""
+    x64 = np.asarray(x, dtype=np.float64).reshape(-1, k)
+    parts = []
+    for aos in (aos_gate, aos_up):
+        w = dequantize(aos, n, k)
+        parts.append((x64 @ w.T, np.abs(x64) @ np.abs(w).T))
+    (g, sg), (u, su) = parts
+    return g, u, sg, su
+
+
+def swiglu_from_parts(parts, tol: float):
+    """Reference ``silu(g) * u`` and error scale ``E`` from ``gate_up_swiglu_parts``."""
+    g, u, sg, su = parts
+    return silu(g) * u, _swiglu_scale(g, u, sg, su, tol)
+
+
 def gate_up_swiglu_entries(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray, n: int,
                            k: int, rows, cols, tol: float):
     """Reference and error scale ``E`` for selected outputs ``(rows[i], cols[i])``."""

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     assert sorted(tq2.EXPORTED_SYMBOLS) == names
     lib = ctypes.CDLL(tq2.LIB_PATH)
     for name in names:
@@ -124,6 +124,29 @@ def test_batched_gemv_checks_before_any_device_work():
     assert b([(0, 0, 0, 0, 0, 128), (0, 0, 0, 0, 0, 256)]) == tq2.TQ2_OK
 
 
+def test_swiglu_checks_before_any_device_work():
+    sw = tq2.gate_up_swiglu_ptr
+    U, X, O = A + 0x40000, A + 0x100000, A + 0x200000
+    assert sw(A, U, X, O, 4, 8, 100) == tq2.TQ2_ERR_SHAPE
+    assert sw(A, U, X, O, 4, 8, 0) == tq2.TQ2_ERR_INVALID
+    assert sw(A, U, X, O, -1, 8, 128) == tq2.TQ2_ERR_INVALID
+    for bad in [(0, U, X, O), (A, 0, X, O), (A, U, 0, O), (A, U, X, 0)]:
+        assert sw(*bad, 4, 8, 128) == tq2.TQ2_ERR_INVALID
+    assert sw(A + 64, U, X, O, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert sw(A, U + 64, X, O, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert sw(A, U, X + 4, O, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert sw(A, U, X, O + 4, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    # out over x, over the gate weight or over the up weight
+    assert sw(A, U, X, X + 16, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert sw(A, U, X, A + 16, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert sw(A, U, X, U + 16, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+    # K beyond the matrix-core kernels' limit (buffers spaced so nothing overlaps)
+    assert sw(A, A + (1 << 24), A + (1 << 25), A + (1 << 27), 4, 8, 1 << 22) == \
+        tq2.TQ2_ERR_INVALID
+    assert sw(0, 0, 0, 0, 0, 8, 128) == tq2.TQ2_OK
+    assert sw(0, 0, 0, 0, 4, 0, 128) == tq2.TQ2_OK
+
+
 def test_device_check_without_gpu():
     """Valid arguments but no gfx950 device: the call must return
     TQ2_ERR_DEVICE (never crash).  Only meaningful where no GPU is visible."""
@@ -132,6 +155,9 @@ def test_device_check_without_gpu():
         pytest.skip("a GPU is visible; this check is for GPU-less hosts")
     st = tq2.gemm_ptr(A, A + 0x100000, 0, A + 0x200000, 4, 8, 128)
     assert st == tq2.TQ2_ERR_DEVICE
+    # gate and up may be the same buffer
+    assert tq2.gate_up_swiglu_ptr(A, A, A + 0x100000, A + 0x200000, 1, 8, 128) == \
+        tq2.TQ2_ERR_DEVICE
     # shared x and weight, distinct outs: valid, so the device check decides
     st = tq2.gemv_batched_ptr([(A, A + 0x100000, 0, A + 0x200000, 8, 128),
                                (A, A + 0x100000, 0, A + 0x200100, 8, 128)])

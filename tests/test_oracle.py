@@ -521,6 +521,18 @@ def test_swiglu_entries_match_full():
     assert np.allclose(e, e_full[rows, cols], rtol=1e-13)
 
 
+def test_swiglu_parts_match_plain_route():
+    n, k = 7, 384
+    c = G.swiglu_case(44, 3, n, k)
+    parts = O.gate_up_swiglu_parts(c["gate"], c["up"], c["x"], n, k)
+    for tol in (1e-5, 2e-3):
+        ref, e = O.swiglu_from_parts(parts, tol)
+        assert np.allclose(ref, O.gate_up_swiglu(c["gate"], c["up"], c["x"], n, k),
+                           rtol=1e-13, atol=1e-15)
+        assert np.allclose(e, O.gate_up_swiglu_error_scale(c["gate"], c["up"], c["x"], n, k, tol),
+                           rtol=1e-13)
+
+
 def _mutant_swiglu(kind):
     def silu(z):
         z = np.asarray(z, np.float64)

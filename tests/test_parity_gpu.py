@@ -338,3 +338,140 @@ def test_gemm_precise_config3_m100(tq2):
 
 def test_gemm_precise_config4(tq2):
     assert_case(tq2, dict(G.config4(), name="config4_precise"), precise=True)
+
+
+# ---------------------------------------------------------------------------
+# tq2_gate_up_swiglu: silu(x W_gate^T) * (x W_up^T), both projections fused.
+# ---------------------------------------------------------------------------
+
+from tests.parity import check_swiglu  # noqa: E402
+
+
+def run_swiglu(tq2, case):
+    m, n, k = case["m"], case["n"], case["k"]
+    gs = upload_weight(tq2, case["gate"], n, k)
+    us = gs if case.get("same") else upload_weight(tq2, case["up"], n, k)
+    x = _dev(case["x"].reshape(m, k))
+    y = tq2.gate_up_swiglu(gs, us, x, n, k)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().reshape(m, n)
+
+
+def swiglu_path(tq2, m, n, k):
+    return tq2.gemm_path(m, n, k)
+
+
+def assert_swiglu(tq2, case):
+    print("swiglu case", case["name"], flush=True)
+    m, n, k = case["m"], case["n"], case["k"]
+    up = case["gate"] if case.get("same") else case["up"]
+    got = run_swiglu(tq2, case)
+    path = swiglu_path(tq2, m, n, k)
+    ref = oracle.gate_up_swiglu(case["gate"], up, case["x"], n, k)
+    e = oracle.gate_up_swiglu_error_scale(case["gate"], up, case["x"], n, k,
+                                          {0: 1e-5, 1: 1e-5, 2: 2e-3}[path])
+    ok, msg = check_swiglu(got, ref, e, path, case["name"])
+    print(msg, flush=True)
+    assert ok, msg
+    return got, ref
+
+
+SWIGLU_GEMV_SHAPES = [(1, 128), (5, 256), (63, 384), (64, 1024), (300, 4096), (77, 12288),
+                      (40, 20480)]
+
+
+@pytest.mark.parametrize("n,k", SWIGLU_GEMV_SHAPES)
+def test_swiglu_decode_shapes(tq2, n, k):
+    assert_swiglu(tq2, G.swiglu_case(4000 + n + k, 1, n, k))
+
+
+# M = 2..16: split-binary16 kernel; 17..128: 16-column-group kernels; > 128
+# with K <= 12288: the ping-pong kernel; K > 12288: the wide-tile kernel.
+SWIGLU_GEMM_SHAPES = [(2, 17, 128), (9, 100, 384), (16, 257, 1024), (17, 33, 256),
+                      (40, 130, 640), (64, 96, 384), (100, 191, 1024), (129, 191, 384),
+                      (200, 97, 768), (300, 1000, 1152), (150, 50, 12416)]
+
+
+@pytest.mark.parametrize("m,n,k", SWIGLU_GEMM_SHAPES)
+def test_swiglu_gemm_shapes(tq2, m, n, k):
+    assert_swiglu(tq2, G.swiglu_case(5000 + m + n + k, m, n, k))
+
+
+def test_swiglu_same_weight_and_zero_gate(tq2):
+    c = G.swiglu_case(6001, 40, 72, 512)
+    got, _ = assert_swiglu(tq2, dict(c, same=True, name="same_weight"))
+    assert np.all(got >= 0)                          # silu(u) * u >= 0
+    zg = c["gate"].reshape(-1, 34).copy()
+    zg[:, :32] = 0x55                                # every gate weight 0 -> g = 0 exactly
+    for m in (1, 5, 40, 200):
+        cz = G.swiglu_case(6002 + m, m, 72, 512)
+        got = run_swiglu(tq2, dict(cz, gate=zg.reshape(-1), name="zero_gate_m%d" % m))
+        assert np.all(got == 0), m
+
+
+def test_swiglu_saturated_gate(tq2):
+    # Large scales: |g| reaches the hundreds, so exp(-g) overflows or
+    # vanishes in f32 and silu(g) must come out as 0 or g.
+    for m in (1, 8, 64, 200):
+        c = G.swiglu_case(6100 + m, m, 130, 1024, probs=G.UNIFORM_TERNARY, d_range=(2.0, 4.0))
+        assert_swiglu(tq2, dict(c, name="saturated_m%d" % m))
+
+
+def test_swiglu_feed_forward_workload(tq2):
+    """K = 4096 -> N = 11008 at M = 1 (GEMV), 7 (split-binary16) and 100
+    (binary16 matrix cores); the reference rows are the first M rows of one
+    oracle evaluation over 100 activation rows (rows are independent)."""
+    gate, up = G.swiglu_weights()
+    n, k = G.SWIGLU_N, G.SWIGLU_K
+    x = G.swiglu_activations(100)
+    parts = oracle.gate_up_swiglu_parts(gate, up, x, n, k)
+    gs, us = upload_weight(tq2, gate, n, k), upload_weight(tq2, up, n, k)
+    for m in (1, 7, 100):
+        print("swiglu workload m", m, flush=True)
+        y = tq2.gate_up_swiglu(gs, us, _dev(x[:m]), n, k)
+        torch.cuda.synchronize()
+        path = tq2.gemm_path(m, n, k)
+        ref, e = oracle.swiglu_from_parts(parts, {0: 1e-5, 1: 1e-5, 2: 2e-3}[path])
+        ok, msg = check_swiglu(y.cpu().numpy(), ref[:m], e[:m], path, "workload m%d" % m)
+        print(msg, flush=True)
+        assert ok, msg
+
+
+def test_swiglu_feed_forward_m1536_sampled(tq2):
+    """K = 4096 -> N = 11008 at M = 1536 (the ping-pong kernel at full size):
+    every column of 64 sampled rows, and 4096 scattered outputs."""
+    gate, up = G.swiglu_weights()
+    n, k, m = G.SWIGLU_N, G.SWIGLU_K, 1536
+    x = G.swiglu_activations(m)
+    gs, us = upload_weight(tq2, gate, n, k), upload_weight(tq2, up, n, k)
+    got = tq2.gate_up_swiglu(gs, us, _dev(x), n, k)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    rng = np.random.default_rng(77)
+    rows = np.sort(rng.choice(m, size=64, replace=False))
+    ref, e = oracle.swiglu_from_parts(oracle.gate_up_swiglu_parts(gate, up, x[rows], n, k), 2e-3)
+    ok, msg = check_swiglu(got[rows], ref, e, 2, "m1536 rows")
+    print(msg, flush=True)
+    assert ok, msg
+    ri, ci = rng.integers(0, m, 4096), rng.integers(0, n, 4096)
+    ref, e = oracle.gate_up_swiglu_entries(gate, up, x, n, k, ri, ci, 2e-3)
+    ok, msg = check_swiglu(got[ri, ci], ref, e, 2, "m1536 scattered")
+    print(msg, flush=True)
+    assert ok, msg
+
+
+def test_swiglu_error_codes_with_device_pointers(tq2):
+    c = G.swiglu_case(6200, 4, 64, 256)
+    gs = upload_weight(tq2, c["gate"], 64, 256)
+    us = upload_weight(tq2, c["up"], 64, 256)
+    x = _dev(c["x"])
+    out = torch.empty((4, 64), dtype=torch.float32, device="cuda")
+    sw = tq2.gate_up_swiglu_ptr
+    assert sw(gs.data_ptr(), us.data_ptr(), x.data_ptr(), out.data_ptr(), 4, 64, 200) == \
+        tq2.TQ2_ERR_SHAPE
+    assert sw(gs.data_ptr(), us.data_ptr(), x.data_ptr(), x.data_ptr(), 4, 64, 256) == \
+        tq2.TQ2_ERR_ALIAS
+    assert sw(gs.data_ptr(), us.data_ptr() + 16, x.data_ptr(), out.data_ptr(), 4, 64, 256) == \
+        tq2.TQ2_ERR_ALIGN
+    assert sw(gs.data_ptr(), us.data_ptr(), x.data_ptr(), out.data_ptr(), 4, 64, 256) == tq2.TQ2_OK
+    torch.cuda.synchronize()

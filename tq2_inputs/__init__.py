@@ -192,11 +192,21 @@ SWIGLU_K, SWIGLU_N = 4096, 11008
 SWIGLU_WEIGHT_SEED = 33
 
 
-def swiglu_workload(m: int):
-    """Gate/up weights of the feed-forward workload and ``m`` activation rows."""
+def swiglu_weights():
+    """Gate and up weights of the feed-forward workload (AoS bytes)."""
     rng = np.random.default_rng(SWIGLU_WEIGHT_SEED)
     gate = make_weight(rng, SWIGLU_N, SWIGLU_K, HALF_ZERO_TERNARY, (0.005, 0.05))
     up = make_weight(rng, SWIGLU_N, SWIGLU_K, HALF_ZERO_TERNARY, (0.005, 0.05))
-    x = make_activations(np.random.default_rng(SWIGLU_WEIGHT_SEED + 1 + m), m, SWIGLU_K)
+    return gate, up
+
+
+def swiglu_activations(m: int) -> np.ndarray:
+    """``m`` activation rows of the feed-forward workload, x ~ N(0, 1)."""
+    return make_activations(np.random.default_rng(SWIGLU_WEIGHT_SEED + 1 + m), m, SWIGLU_K)
+
+
+def swiglu_workload(m: int):
+    """Gate/up weights of the feed-forward workload and ``m`` activation rows."""
+    gate, up = swiglu_weights()
     return dict(name=f"swiglu_m{m}_k{SWIGLU_K}_n{SWIGLU_N}", m=m, n=SWIGLU_N, k=SWIGLU_K,
-                gate=gate, up=up, x=x)
+                gate=gate, up=up, x=swiglu_activations(m))
