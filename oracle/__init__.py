@@ -28,3 +28,13 @@ from .tq2_oracle import (  # noqa: F401
     silu,
     swiglu_from_parts,
 )
+from .q1_oracle import (  # noqa: F401,E402
+    Q1_BLOCK_BYTES,
+    Q1_BLOCK_WEIGHTS,
+    bit_of,
+    dequantize_block_scalar_q1,
+    dequantize_q1,
+    dequantize_scalar_q1,
+    matmul_scalar_q1,
+    q1_aos_bytes,
+)

@@ -195,21 +195,34 @@ def dequantize(aos: np.ndarray, n: int, k: int, rows=None) -> np.ndarray:
     return w.reshape(w.shape[0], -1)
 
 
-def matmul(aos: np.ndarray, x: np.ndarray, n: int, k: int, residual=None) -> np.ndarray:
+def _dequantizer(fmt: str):
+    """Weight decoder for a format: "tq2" (TQ2_0_g128, this module) or "q1"
+    (Q1_g128, ``q1_oracle``)."""
+    if fmt == "tq2":
+        return dequantize
+    if fmt == "q1":
+        from .q1_oracle import dequantize_q1
+        return dequantize_q1
+    raise ValueError("unknown weight format %r" % (fmt,))
+
+
+def matmul(aos: np.ndarray, x: np.ndarray, n: int, k: int, residual=None,
+           fmt: str = "tq2") -> np.ndarray:
     """float64 ``out = residual + x @ W^T`` (unrounded)."""
     x64 = np.asarray(x, dtype=np.float64).reshape(-1, k)
-    w = dequantize(aos, n, k)
+    w = _dequantizer(fmt)(aos, n, k)
     out = x64 @ w.T
     if residual is not None:
         out = np.asarray(residual, dtype=np.float64).reshape(out.shape) + out
     return out
 
 
-def error_scale(aos: np.ndarray, x: np.ndarray, n: int, k: int, residual=None) -> np.ndarray:
+def error_scale(aos: np.ndarray, x: np.ndarray, n: int, k: int, residual=None,
+                fmt: str = "tq2") -> np.ndarray:
     """``S[m, n] = sum_k |x[m, k] * w[n, k]|`` (+ ``|residual[m, n]|`` when a
     residual is added: it is one more term of the same sum)."""
     x64 = np.abs(np.asarray(x, dtype=np.float64).reshape(-1, k))
-    w = np.abs(dequantize(aos, n, k))
+    w = np.abs(_dequantizer(fmt)(aos, n, k))
     s = x64 @ w.T
     if residual is not None:
         s = s + np.abs(np.asarray(residual, dtype=np.float64).reshape(s.shape))
@@ -217,14 +230,14 @@ def error_scale(aos: np.ndarray, x: np.ndarray, n: int, k: int, residual=None) -
 
 
 def matmul_entries(aos: np.ndarray, x: np.ndarray, n: int, k: int, rows, cols,
-                   residual=None):
+                   residual=None, fmt: str = "tq2"):
     """Reference and error scale for selected outputs ``(rows[i], cols[i])``,
     each computed on its own (for spot checks of full-size runs)."""
     rows = np.asarray(rows)
     cols = np.asarray(cols)
     x64 = np.asarray(x, dtype=np.float64).reshape(-1, k)
     ucols, inv = np.unique(cols, return_inverse=True)
-    w = dequantize(aos, n, k, rows=ucols)                               # [u, k]
+    w = _dequantizer(fmt)(aos, n, k, rows=ucols)                        # [u, k]
     wi = w[inv]                                                         # [s, k]
     xi = x64[rows]                                                      # [s, k]
     ref = np.sum(xi * wi, axis=1)
@@ -236,11 +249,12 @@ def matmul_entries(aos: np.ndarray, x: np.ndarray, n: int, k: int, rows, cols,
     return ref, s
 
 
-def matmul_rows(aos: np.ndarray, x: np.ndarray, n: int, k: int, cols, residual=None):
+def matmul_rows(aos: np.ndarray, x: np.ndarray, n: int, k: int, cols, residual=None,
+                fmt: str = "tq2"):
     """Reference and error scale for all rows of ``x`` at output columns ``cols``."""
     cols = np.asarray(cols)
     x64 = np.asarray(x, dtype=np.float64).reshape(-1, k)
-    w = dequantize(aos, n, k, rows=cols)
+    w = _dequantizer(fmt)(aos, n, k, rows=cols)
     ref = x64 @ w.T
     s = np.abs(x64) @ np.abs(w).T
     if residual is not None:
@@ -267,10 +281,10 @@ def silu(z):
 
 
 def gate_up_swiglu(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray, n: int,
-                   k: int) -> np.ndarray:
+                   k: int, fmt: str = "tq2") -> np.ndarray:
     """float64 ``silu(x @ W_gate^T) * (x @ W_up^T)``, shape ``[M, n]``."""
-    g = matmul(aos_gate, x, n, k)
-    u = matmul(aos_up, x, n, k)
+    g = matmul(aos_gate, x, n, k, fmt=fmt)
+    u = matmul(aos_up, x, n, k, fmt=fmt)
     return silu(g) * u
 
 
@@ -283,24 +297,24 @@ def _swiglu_scale(g, u, sg, su, tol):
 
 
 def gate_up_swiglu_error_scale(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray,
-                               n: int, k: int, tol: float) -> np.ndarray:
+                               n: int, k: int, tol: float, fmt: str = "tq2") -> np.ndarray:
     """Scale ``E`` such that projections each within ``tol * sum_k |x w|`` of
     the exact values give an output within ``tol * E`` of the exact one."""
-    g = matmul(aos_gate, x, n, k)
-    u = matmul(aos_up, x, n, k)
-    sg = error_scale(aos_gate, x, n, k)
-    su = error_scale(aos_up, x, n, k)
+    g = matmul(aos_gate, x, n, k, fmt=fmt)
+    u = matmul(aos_up, x, n, k, fmt=fmt)
+    sg = error_scale(aos_gate, x, n, k, fmt=fmt)
+    su = error_scale(aos_up, x, n, k, fmt=fmt)
     return _swiglu_scale(g, u, sg, su, tol)
 
 
 def gate_up_swiglu_parts(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray, n: int,
-                         k: int):
+                         k: int, fmt: str = "tq2"):
     """``(g, u, Sg, Su)``: both projections and their ``sum_k |x w|`` scales,
     each weight decoded once (for large cases)."""
     x64 = np.asarray(x, dtype=np.float64).reshape(-1, k)
     parts = []
     for aos in (aos_gate, aos_up):
-        w = dequantize(aos, n, k)
+        w = _dequantizer(fmt)(aos, n, k)
         parts.append((x64 @ w.T, np.abs(x64) @ np.abs(w).T))
     (g, sg), (u, su) = parts
     return g, u, sg, su
@@ -313,8 +327,8 @@ def swiglu_from_parts(parts, tol: float):
 
 
 def gate_up_swiglu_entries(aos_gate: np.ndarray, aos_up: np.ndarray, x: np.ndarray, n: int,
-                           k: int, rows, cols, tol: float):
+                           k: int, rows, cols, tol: float, fmt: str = "tq2"):
     """Reference and error scale ``E`` for selected outputs ``(rows[i], cols[i])``."""
-    g, sg = matmul_entries(aos_gate, x, n, k, rows, cols)
-    u, su = matmul_entries(aos_up, x, n, k, rows, cols)
+    g, sg = matmul_entries(aos_gate, x, n, k, rows, cols, fmt=fmt)
+    u, su = matmul_entries(aos_up, x, n, k, rows, cols, fmt=fmt)
     return silu(g) * u, _swiglu_scale(g, u, sg, su, tol)

@@ -562,3 +562,193 @@ def test_pins_catch_planted_swiglu_mistakes(kind):
     silu, sw = _mutant_swiglu(kind)
     results = [pin_silu_values(silu), pin_swiglu_hand_worked(sw), pin_swiglu_structure(sw)]
     assert not all(results), kind
+
+
+# ---------------------------------------------------------------------------
+# Q1_g128 (1-bit sibling format).  The pages name the q1 kernels but print no
+# layout; the pins hold the oracle to the recorded convention (18-byte block:
+# qs[16] then a little-endian binary16 d; bit j = (qs[j // 8] >> (j % 8)) & 1;
+# set -> +d, clear -> -d).
+# ---------------------------------------------------------------------------
+
+from oracle import q1_oracle as Q  # noqa: E402
+
+
+def q1_block(qs_bytes, d_bits):
+    qs = bytes(qs_bytes)
+    assert len(qs) == 16
+    return qs + bytes([d_bits & 0xFF, (d_bits >> 8) & 0xFF])
+
+
+def _q1(b):
+    return np.frombuffer(b, np.uint8)
+
+
+def pin_q1_hand_worked(deq):
+    # qs[0] = 0x05 -> bits 1, 0, 1, 0, 0, 0, 0, 0 (LSB first); every other bit
+    # clear; d = 0.5 -> +0.5, -0.5, +0.5, then -0.5 for weights 3..127.
+    w = deq(_q1(q1_block([0x05] + [0x00] * 15, 0x3800)), 1, 128)[0]
+    want = np.full(128, -0.5)
+    want[0] = want[2] = 0.5
+    ok = np.array_equal(w, want)
+    # qs[15] = 0x7F, every other byte 0xFF; d = -2 -> -2 everywhere except
+    # weight 127 (bit 7 of byte 15, clear) = +2.
+    w = deq(_q1(q1_block([0xFF] * 15 + [0x7F], 0xC000)), 1, 128)[0]
+    want = np.full(128, -2.0)
+    want[127] = 2.0
+    ok &= np.array_equal(w, want)
+    return bool(ok)
+
+
+def pin_q1_unit_vectors(deq):
+    # One block per position j with only bit j set (numpy's little-endian
+    # bit packing locates it, independent of the oracle's shift-and-mask).
+    ok = True
+    for j in range(128):
+        bits = np.zeros(128, dtype=np.uint8)
+        bits[j] = 1
+        qs = np.packbits(bits, bitorder="little")
+        w = deq(_q1(q1_block(qs.tolist(), ONE)), 1, 128)[0]
+        want = np.full(128, -1.0)
+        want[j] = 1.0
+        ok &= np.array_equal(w, want)
+    return bool(ok)
+
+
+def pin_q1_two_block_row(mm):
+    # x[k] = k + 1 (K = 256).  Block 0: d = 1, every bit set but weight 0:
+    # 8256 - 2 * 1 = 8254.  Block 1: d = 0.25, every bit clear but weight 127
+    # (k = 255): 0.25 * (-24640 + 2 * 256) = -6032.  Total 2222.
+    b0 = q1_block([0xFE] + [0xFF] * 15, ONE)
+    b1 = q1_block([0x00] * 15 + [0x80], 0x3400)
+    x = (np.arange(256, dtype=np.float32) + 1.0)[None, :]
+    return float(mm(_q1(b0 + b1), x, 1, 256)[0, 0]) == 2222.0
+
+
+def pin_q1_closed_forms(mm):
+    n, k = 5, 384
+    c = G.random_case_q1(31, 3, n, k)
+    aos, x = c["aos"], c["x"]
+    a = aos.reshape(n, k // 128, 18)
+    d = (a[:, :, 16].astype(np.uint16) | (a[:, :, 17].astype(np.uint16) << 8)).view(
+        np.float16).astype(np.float64)
+    blocksum = x.astype(np.float64).reshape(3, k // 128, 128).sum(axis=2)
+    plus = blocksum @ d.T
+
+    def with_bits(v):
+        b = a.copy()
+        b[:, :, :16] = v
+        return b.reshape(-1)
+    ok = np.allclose(mm(with_bits(0xFF), x, n, k), plus, rtol=1e-13, atol=0)
+    ok &= np.allclose(mm(with_bits(0x00), x, n, k), -plus, rtol=1e-13, atol=0)
+    # complementing every bit negates the output; the residual is added once
+    comp = a.copy()
+    comp[:, :, :16] ^= 0xFF
+    base = mm(aos, x, n, k)
+    ok &= np.allclose(mm(comp.reshape(-1), x, n, k), -base, rtol=1e-13, atol=1e-13)
+    r = np.random.default_rng(3).standard_normal((3, n))
+    ok &= np.allclose(mm(aos, x, n, k, r) - base, r, rtol=0, atol=1e-12)
+    zero = a.copy()
+    zero[:, :, 16:] = 0
+    ok &= np.array_equal(mm(zero.reshape(-1), x, n, k), np.zeros((3, n)))
+    return bool(ok)
+
+
+def pin_q1_scalar_loop(mm):
+    ok = True
+    for seed, (m, n, k) in enumerate([(1, 1, 128), (2, 3, 256), (3, 2, 384)]):
+        c = G.random_case_q1(200 + seed, m, n, k, residual=True)
+        ref = np.array(Q.matmul_scalar_q1(bytes(c["aos"]), c["x"].tolist(), n, k,
+                                          c["residual"].tolist()))
+        ok &= np.allclose(mm(c["aos"], c["x"], n, k, c["residual"]), ref, rtol=1e-12,
+                          atol=1e-12)
+    return bool(ok)
+
+
+def _q1_mm(aos, x, n, k, residual=None):
+    return O.matmul(aos, x, n, k, residual, fmt="q1")
+
+
+def test_q1_block_size():
+    assert Q.Q1_BLOCK_BYTES == 18 and Q.q1_aos_bytes(1, 128) == 18
+    assert Q.q1_aos_bytes(4096, 4096) == 131072 * 18          # 2,359,296 B
+
+
+def test_q1_hand_worked_blocks():
+    assert pin_q1_hand_worked(Q.dequantize_q1)
+
+    def deq_scalar(aos, n, k):
+        return np.array(Q.dequantize_scalar_q1(bytes(aos), n, k))
+    assert pin_q1_hand_worked(deq_scalar)
+    assert pin_q1_unit_vectors(deq_scalar)
+
+
+def test_q1_unit_vectors():
+    assert pin_q1_unit_vectors(Q.dequantize_q1)
+
+
+def test_q1_two_block_row_and_closed_forms():
+    assert pin_q1_two_block_row(_q1_mm)
+    assert pin_q1_closed_forms(_q1_mm)
+
+
+def test_q1_matches_scalar_triple_loop():
+    assert pin_q1_scalar_loop(_q1_mm)
+
+
+def test_q1_entries_rows_and_swiglu_use_the_q1_decoder():
+    n, k = 9, 256
+    c = G.random_case_q1(210, 5, n, k, residual=True)
+    full = O.matmul(c["aos"], c["x"], n, k, c["residual"], fmt="q1")
+    rows, cols = np.array([0, 4, 2]), np.array([8, 0, 3])
+    ref, _ = O.matmul_entries(c["aos"], c["x"], n, k, rows, cols, c["residual"], fmt="q1")
+    assert np.allclose(ref, full[rows, cols], rtol=1e-13, atol=1e-13)
+    ref2, _ = O.matmul_rows(c["aos"], c["x"], n, k, [1, 7], c["residual"], fmt="q1")
+    assert np.allclose(ref2, full[:, [1, 7]], rtol=1e-13, atol=1e-13)
+    s = G.swiglu_case_q1(211, 3, n, k)
+    g = O.matmul(s["gate"], s["x"], n, k, fmt="q1")
+    u = O.matmul(s["up"], s["x"], n, k, fmt="q1")
+    assert np.allclose(O.gate_up_swiglu(s["gate"], s["up"], s["x"], n, k, fmt="q1"),
+                       g * expit(g) * u, rtol=1e-12, atol=1e-15)
+    with pytest.raises(ValueError):
+        O.matmul(c["aos"], c["x"], n, k, fmt="q2")
+
+
+def _mutant_q1(kind):
+    def deq(aos, n, k, rows=None):
+        blk = Q._blocks_q1(aos, n, k)
+        qs = blk[:, :, :16]
+        lo, hi = blk[:, :, 16].astype(np.uint16), blk[:, :, 17].astype(np.uint16)
+        bits = lo | (hi << 8)
+        if kind == "scale_big_endian":
+            bits = hi | (lo << 8)
+        d = O.f16_bits_to_float_array(bits)
+        w = np.empty(qs.shape[:2] + (128,))
+        for j in range(128):
+            if kind == "msb_first":
+                b = (qs[:, :, j >> 3] >> (7 - (j & 7))) & 1
+            elif kind == "strided":
+                b = (qs[:, :, j & 15] >> (j >> 4)) & 1
+            else:
+                b = (qs[:, :, j >> 3] >> (j & 7)) & 1
+            val = np.where(b == 1, 1.0, -1.0)
+            if kind == "sign_swapped":
+                val = -val
+            if kind == "zero_for_clear":
+                val = np.where(b == 1, 1.0, 0.0)
+            w[:, :, j] = val * (1.0 if kind == "scale_dropped" else d)
+        return w.reshape(w.shape[0], -1)
+    return deq
+
+
+@pytest.mark.parametrize("kind", ["msb_first", "strided", "sign_swapped", "zero_for_clear",
+                                  "scale_dropped", "scale_big_endian"])
+def test_pins_catch_planted_q1_mistakes(kind):
+    deq = _mutant_q1(kind)
+
+    def mm(aos, x, n, k, residual=None):
+        out = np.asarray(x, np.float64).reshape(-1, k) @ deq(aos, n, k).T
+        return out if residual is None else np.asarray(residual, np.float64) + out
+    results = [pin_q1_hand_worked(deq), pin_q1_unit_vectors(deq), pin_q1_two_block_row(mm),
+               pin_q1_closed_forms(mm), pin_q1_scalar_loop(mm)]
+    assert not all(results), kind

@@ -210,3 +210,69 @@ def swiglu_workload(m: int):
     gate, up = swiglu_weights()
     return dict(name=f"swiglu_m{m}_k{SWIGLU_K}_n{SWIGLU_N}", m=m, n=SWIGLU_N, k=SWIGLU_K,
                 gate=gate, up=up, x=swiglu_activations(m))
+
+
+# ---------------------------------------------------------------------------
+# Q1_g128 (1-bit sibling format): blocks of 128 weights, 16 bytes of bits then
+# a little-endian binary16 scale (18 bytes).  Bits are drawn i.i.d. fair, so
+# the draw does not depend on the bit-order convention either.
+# ---------------------------------------------------------------------------
+
+Q1_BLOCK_BYTES = 18
+Q1_CODE_BYTES = 16
+
+
+def make_weight_q1(rng: np.random.Generator, n: int, k: int,
+                   d_range=(0.01, 0.1)) -> np.ndarray:
+    """A random out-major ``[n, k]`` Q1_g128 weight as flat AoS bytes."""
+    if k % BLOCK_WEIGHTS:
+        raise ValueError("k must be a multiple of 128")
+    nblk = n * (k // BLOCK_WEIGHTS)
+    bits = rng.integers(0, 256, size=nblk * Q1_CODE_BYTES, dtype=np.uint8)
+    scales = draw_scales_f16(rng, nblk, *d_range)
+    blocks = np.empty((nblk, Q1_BLOCK_BYTES), dtype=np.uint8)
+    blocks[:, :Q1_CODE_BYTES] = bits.reshape(nblk, Q1_CODE_BYTES)
+    blocks[:, Q1_CODE_BYTES:] = scales.astype("<f2").view(np.uint8).reshape(nblk, 2)
+    return blocks.reshape(-1)
+
+
+def random_case_q1(seed: int, m: int, n: int, k: int, d_range=(0.01, 0.1),
+                   residual: bool = False, outlier_frac: float = 0.0):
+    """A generic seeded Q1_g128 case for shape sweeps and edge cases."""
+    rng = np.random.default_rng(seed)
+    w = make_weight_q1(rng, n, k, d_range)
+    x = make_activations(rng, m, k, outlier_frac=outlier_frac)
+    r = rng.standard_normal((m, n), dtype=np.float32) if residual else None
+    return dict(name=f"q1_s{seed}_m{m}_n{n}_k{k}", m=m, n=n, k=k, aos=w, x=x, residual=r)
+
+
+Q1_SEEDS = {"decode": 21, "gemm": 24}
+
+
+def q1_decode(with_residual: bool = True):
+    """Q1 decode GEMV, M=1, K=N=4096 (131072 blocks, 2.36 MB), d ~ U[0.01, 0.1]."""
+    rng = np.random.default_rng(Q1_SEEDS["decode"])
+    n = k = 4096
+    w = make_weight_q1(rng, n, k, (0.01, 0.1))
+    x = make_activations(rng, 1, k)
+    r = rng.standard_normal((1, n), dtype=np.float32)
+    return dict(name="q1_gemv_m1_k4096_n4096" + ("_residual" if with_residual else ""),
+                m=1, n=n, k=k, aos=w, x=x, residual=r if with_residual else None)
+
+
+def q1_gemm():
+    """Q1 large-M GEMM, M=1536, K=N=3072, x ~ N(0, 1) with 1% outliers x20."""
+    rng = np.random.default_rng(Q1_SEEDS["gemm"])
+    m, n, k = 1536, 3072, 3072
+    w = make_weight_q1(rng, n, k, (0.01, 0.1))
+    x = make_activations(rng, m, k, outlier_frac=0.01, outlier_mult=20.0)
+    return dict(name="q1_gemm_m1536_k3072_n3072", m=m, n=n, k=k, aos=w, x=x, residual=None)
+
+
+def swiglu_case_q1(seed: int, m: int, n: int, k: int, d_range=(0.005, 0.05)):
+    """Q1 gate and up weights (both ``[n, k]``) and activations ``[m, k]``."""
+    rng = np.random.default_rng(seed)
+    gate = make_weight_q1(rng, n, k, d_range)
+    up = make_weight_q1(rng, n, k, d_range)
+    x = make_activations(rng, m, k)
+    return dict(name=f"q1_swiglu_s{seed}_m{m}_n{n}_k{k}", m=m, n=n, k=k, gate=gate, up=up, x=x)
