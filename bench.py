@@ -42,6 +42,8 @@ def parse():
                    help="skip the 100-layer M=1536 chain (config 5)")
     p.add_argument("--no-swiglu", action="store_true",
                    help="skip the fused gate/up + SwiGLU lines (K=4096 -> N=11008)")
+    p.add_argument("--no-q1", action="store_true",
+                   help="skip the Q1_g128 (1-bit) decode GEMV and M=1536 GEMM lines")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device-to-device copy of this size (MiB) so a "
                         "counter run can scale FETCH_SIZE / WRITE_SIZE against known bytes")
@@ -242,6 +244,66 @@ def swiglu_bench(torch, tq2, G, dev, stream, args):
     }
 
 
+def q1_bench(torch, tq2, G, dev, stream, args):
+    """Q1_g128 (1-bit) sibling format on the same shapes as the TQ2 lines:
+    decode GEMV M=1, K=N=4096 with residual (weight copies rotated past the
+    Infinity Cache), and the M=1536, K=N=3072 GEMM."""
+    c = G.q1_decode(True)
+    n, k = c["n"], c["k"]
+    soa = tq2.reformat_aos_to_soa(torch.from_numpy(c["aos"]).to(dev), n, k, fmt="q1")
+    sb = tq2.q1_soa_bytes(n, k)
+    pool = max(1, int(math.ceil(args.pool_mib * 2 ** 20 / sb)))
+    pool_buf = soa.repeat(pool)
+    base = pool_buf.data_ptr()
+    x = torch.from_numpy(c["x"]).to(dev).reshape(-1)
+    res = torch.from_numpy(c["residual"]).to(dev).reshape(-1)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+
+    def gemv_call(i):
+        st = tq2.q1_gemv_ptr(base + (i % pool) * sb, x.data_ptr(), res.data_ptr(), out.data_ptr(),
+                             n, k, torch.cuda.current_stream(dev).cuda_stream)
+        if st != 0:
+            raise RuntimeError("tq2_q1_gemv failed: %s" % tq2.status_string(st))
+
+    gg = capture(torch, stream, gemv_call, pool)
+    time_graph(torch, gg, 2, stream)
+    reps = max(1, int(math.ceil(args.steps / pool)))
+    ms, _ = time_graph(torch, gg, reps, stream)
+    us = ms * 1e3 / (reps * pool)
+    nbytes = n * (k // 128) * 18 + 4 * k + 8 * n
+    gbs = nbytes / (us * 1e-6) / 1e9
+    del gg, pool_buf
+
+    c4 = G.q1_gemm()
+    m4, n4, k4 = c4["m"], c4["n"], c4["k"]
+    soa4 = tq2.reformat_aos_to_soa(torch.from_numpy(c4["aos"]).to(dev), n4, k4, fmt="q1")
+    x4 = torch.from_numpy(c4["x"]).to(dev)
+    out4 = torch.empty((m4, n4), dtype=torch.float32, device=dev)
+
+    def gemm_call(i):
+        st = tq2.q1_gemm_ptr(soa4.data_ptr(), x4.data_ptr(), 0, out4.data_ptr(), m4, n4, k4,
+                             torch.cuda.current_stream(dev).cuda_stream)
+        if st != 0:
+            raise RuntimeError("tq2_q1_gemm failed: %s" % tq2.status_string(st))
+
+    per_graph = 20
+    g4 = capture(torch, stream, gemm_call, per_graph)
+    time_graph(torch, g4, 2, stream)
+    reps4 = max(1, args.gemm_reps // per_graph)
+    ms4, _ = time_graph(torch, g4, reps4, stream)
+    us4 = ms4 * 1e3 / (reps4 * per_graph)
+    tflops = 2.0 * m4 * n4 * k4 / (us4 * 1e-6) / 1e12
+    return {
+        "q1_gemv_k4096_n4096_residual": {
+            "gbs": round(gbs, 2), "us_per_call": round(us, 3), "bytes_per_call": nbytes,
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "calls": reps * pool},
+        "q1_gemm_m1536_k3072_n3072": {
+            "tflops": round(tflops, 2), "us_per_call": round(us4, 3),
+            "peak_tflops": F16_MFMA_PEAK_TFLOPS, "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
+            "path": tq2.gemm_path(m4, n4, k4), "calls": reps4 * per_graph},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -385,6 +447,9 @@ def main():
 
     if not args.no_swiglu:
         result.update(swiglu_bench(torch, tq2, G, dev, stream, args))
+
+    if not args.no_q1:
+        result.update(q1_bench(torch, tq2, G, dev, stream, args))
 
     if not args.no_chain:
         result["chain_100_layers_m1536"] = chain_bench(torch, tq2, G, dev, stream)

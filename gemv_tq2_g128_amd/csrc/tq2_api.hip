@@ -54,22 +54,99 @@ int launch_status(hipError_t e) { return e == hipSuccess ? TQ2_OK : TQ2_ERR_LAUN
 // Host-side checks common to the matmul entry points once the shape is valid
 // and non-empty: pointers, alignment and aliasing.
 int check_matmul_host(const void* soa, const float* x, const float* residual, const float* out,
-                      int64_t m, int64_t n, int64_t k) {
+                      int64_t m, int64_t n, int64_t k, tq2::Fmt f = tq2::Fmt::kTq2) {
   if (!soa || !x || !out) return TQ2_ERR_INVALID;
   if (!aligned(soa, 256) || !aligned(x, 16) || !aligned(out, 16) ||
       (residual && !aligned(residual, 16)))
     return TQ2_ERR_ALIGN;
   const size_t xb = size_t(m) * size_t(k) * 4, ob = size_t(m) * size_t(n) * 4;
-  const size_t sb = tq2::soa_bytes(n, k);
+  const size_t sb = tq2::soa_bytes(f, n, k);
   if (overlaps(out, ob, x, xb) || overlaps(out, ob, soa, sb)) return TQ2_ERR_ALIAS;
   if (residual && residual != out && overlaps(out, ob, residual, ob)) return TQ2_ERR_ALIAS;
   return TQ2_OK;
 }
 
 int check_matmul_args(const void* soa, const float* x, const float* residual, const float* out,
-                      int64_t m, int64_t n, int64_t k) {
-  const int st = check_matmul_host(soa, x, residual, out, m, n, k);
+                      int64_t m, int64_t n, int64_t k, tq2::Fmt f = tq2::Fmt::kTq2) {
+  const int st = check_matmul_host(soa, x, residual, out, m, n, k, f);
   return st != TQ2_OK ? st : check_device();
+}
+
+// The matrix-core kernels' 32-bit offsets (see tq2_internal.h).
+bool gemm_shape_fits(int64_t n, int64_t k) {
+  return k <= tq2::kGemmMaxK && n * (k / 4) < tq2::kGemmMaxCodeBytes;
+}
+
+int reformat_impl(tq2::Fmt f, const void* aos, void* soa, int64_t n, int64_t k, void* stream) {
+  int st = check_shape(0, n, k);
+  if (st != TQ2_OK) return st;
+  if (n == 0) return TQ2_OK;
+  if (!aos || !soa) return TQ2_ERR_INVALID;
+  if (!aligned(aos, 2) || !aligned(soa, 256)) return TQ2_ERR_ALIGN;
+  const size_t ab = size_t(n) * size_t(k / tq2::kBlockWeights) *
+                    (f == tq2::Fmt::kQ1 ? tq2::kQ1BlockBytes : tq2::kBlockBytes);
+  if (overlaps(aos, ab, soa, tq2::soa_bytes(f, n, k))) return TQ2_ERR_ALIAS;
+  st = check_device();
+  if (st != TQ2_OK) return st;
+  const uint16_t* a = static_cast<const uint16_t*>(aos);
+  uint8_t* o = static_cast<uint8_t*>(soa);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch_status(f == tq2::Fmt::kQ1 ? tq2::launch_reformat_q1(a, o, n, k, s)
+                                          : tq2::launch_reformat(a, o, n, k, s));
+}
+
+int gemv_impl(tq2::Fmt f, const void* soa, const float* x, const float* residual, float* out,
+              int64_t n, int64_t k, void* stream) {
+  int st = check_shape(1, n, k);
+  if (st != TQ2_OK) return st;
+  if (n == 0) return TQ2_OK;
+  st = check_matmul_args(soa, x, residual, out, 1, n, k, f);
+  if (st != TQ2_OK) return st;
+  const uint8_t* w = static_cast<const uint8_t*>(soa);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch_status(f == tq2::Fmt::kQ1 ? tq2::launch_gemv_q1(w, x, residual, out, n, k, s)
+                                          : tq2::launch_gemv(w, x, residual, out, n, k, s));
+}
+
+// path: 0 = GEMV, 1 = split-binary16 matrix cores, 2 = binary16 matrix cores.
+int gemm_impl(tq2::Fmt f, int path, const void* soa, const float* x, const float* residual,
+              float* out, int64_t m, int64_t n, int64_t k, void* stream) {
+  if (path == 0) return gemv_impl(f, soa, x, residual, out, n, k, stream);
+  int st = check_matmul_host(soa, x, residual, out, m, n, k, f);
+  if (st != TQ2_OK) return st;
+  if (!gemm_shape_fits(n, k)) return TQ2_ERR_INVALID;
+  st = check_device();
+  if (st != TQ2_OK) return st;
+  const uint8_t* w = static_cast<const uint8_t*>(soa);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch_status(f == tq2::Fmt::kQ1
+                           ? tq2::launch_gemm_q1(path, w, x, residual, out, m, n, k, s)
+                           : tq2::launch_gemm(path, w, x, residual, out, m, n, k, s));
+}
+
+int swiglu_impl(tq2::Fmt f, const void* gate_soa, const void* up_soa, const float* x,
+                float* out, int64_t m, int64_t n, int64_t k, void* stream) {
+  int st = check_shape(m, n, k);
+  if (st != TQ2_OK) return st;
+  if (m == 0 || n == 0) return TQ2_OK;
+  if (!up_soa) return TQ2_ERR_INVALID;
+  st = check_matmul_host(gate_soa, x, nullptr, out, m, n, k, f);
+  if (st != TQ2_OK) return st;
+  if (!aligned(up_soa, 256)) return TQ2_ERR_ALIGN;
+  if (overlaps(out, size_t(m) * size_t(n) * 4, up_soa, tq2::soa_bytes(f, n, k)))
+    return TQ2_ERR_ALIAS;
+  const int path = m <= 1 ? 0 : (m <= tq2::kSplitMaxM ? 1 : 2);
+  if (path != 0 && !gemm_shape_fits(n, k)) return TQ2_ERR_INVALID;
+  st = check_device();
+  if (st != TQ2_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* g = static_cast<const uint8_t*>(gate_soa);
+  const uint8_t* u = static_cast<const uint8_t*>(up_soa);
+  if (f == tq2::Fmt::kQ1)
+    return launch_status(path == 0 ? tq2::launch_gemv_swiglu_q1(g, u, x, out, n, k, s)
+                                   : tq2::launch_gemm_swiglu_q1(path, g, u, x, out, m, n, k, s));
+  return launch_status(path == 0 ? tq2::launch_gemv_swiglu(g, u, x, out, n, k, s)
+                                 : tq2::launch_gemm_swiglu(path, g, u, x, out, m, n, k, s));
 }
 
 }  // namespace
@@ -89,17 +166,7 @@ size_t tq2_soa_bytes(int64_t n, int64_t k) {
 int tq2_soa_layout_version(void) { return tq2::kLayoutVersion; }
 
 int tq2_reformat_aos_to_soa(const void* aos, void* soa, int64_t n, int64_t k, void* stream) {
-  int st = check_shape(0, n, k);
-  if (st != TQ2_OK) return st;
-  if (n == 0) return TQ2_OK;
-  if (!aos || !soa) return TQ2_ERR_INVALID;
-  if (!aligned(aos, 2) || !aligned(soa, 256)) return TQ2_ERR_ALIGN;
-  if (overlaps(aos, tq2_aos_bytes(n, k), soa, tq2::soa_bytes(n, k))) return TQ2_ERR_ALIAS;
-  st = check_device();
-  if (st != TQ2_OK) return st;
-  return launch_status(tq2::launch_reformat(static_cast<const uint16_t*>(aos),
-                                            static_cast<uint8_t*>(soa), n, k,
-                                            static_cast<hipStream_t>(stream)));
+  return reformat_impl(tq2::Fmt::kTq2, aos, soa, n, k, stream);
 }
 
 int tq2_gemm_path(int64_t m, int64_t n, int64_t k) {
@@ -111,13 +178,7 @@ int tq2_gemm_path(int64_t m, int64_t n, int64_t k) {
 
 int tq2_gemv(const void* soa, const float* x, const float* residual, float* out, int64_t n,
              int64_t k, void* stream) {
-  int st = check_shape(1, n, k);
-  if (st != TQ2_OK) return st;
-  if (n == 0) return TQ2_OK;
-  st = check_matmul_args(soa, x, residual, out, 1, n, k);
-  if (st != TQ2_OK) return st;
-  return launch_status(tq2::launch_gemv(static_cast<const uint8_t*>(soa), x, residual, out, n,
-                                        k, static_cast<hipStream_t>(stream)));
+  return gemv_impl(tq2::Fmt::kTq2, soa, x, residual, out, n, k, stream);
 }
 
 int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream) {
@@ -177,61 +238,55 @@ int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream) 
 
 int tq2_gemm(const void* soa, const float* x, const float* residual, float* out, int64_t m,
              int64_t n, int64_t k, void* stream) {
-  int st = check_shape(m, n, k);
+  const int st = check_shape(m, n, k);
   if (st != TQ2_OK) return st;
   if (m == 0 || n == 0) return TQ2_OK;
-  st = check_matmul_args(soa, x, residual, out, m, n, k);
-  if (st != TQ2_OK) return st;
-  const int path = tq2_gemm_path(m, n, k);
-  if (path != 0 && (k > tq2::kGemmMaxK || n * (k / 4) >= tq2::kGemmMaxCodeBytes))
-    return TQ2_ERR_INVALID;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (path == 0)
-    return launch_status(
-        tq2::launch_gemv(static_cast<const uint8_t*>(soa), x, residual, out, n, k, s));
-  return launch_status(
-      tq2::launch_gemm(path, static_cast<const uint8_t*>(soa), x, residual, out, m, n, k, s));
+  return gemm_impl(tq2::Fmt::kTq2, tq2_gemm_path(m, n, k), soa, x, residual, out, m, n, k, stream);
 }
 
 int tq2_gemm_precise(const void* soa, const float* x, const float* residual, float* out,
                      int64_t m, int64_t n, int64_t k, void* stream) {
-  int st = check_shape(m, n, k);
+  const int st = check_shape(m, n, k);
   if (st != TQ2_OK) return st;
   if (m == 0 || n == 0) return TQ2_OK;
-  st = check_matmul_args(soa, x, residual, out, m, n, k);
-  if (st != TQ2_OK) return st;
-  const int path = m <= 1 ? 0 : 1;
-  if (path != 0 && (k > tq2::kGemmMaxK || n * (k / 4) >= tq2::kGemmMaxCodeBytes))
-    return TQ2_ERR_INVALID;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (path == 0)
-    return launch_status(
-        tq2::launch_gemv(static_cast<const uint8_t*>(soa), x, residual, out, n, k, s));
-  return launch_status(
-      tq2::launch_gemm(path, static_cast<const uint8_t*>(soa), x, residual, out, m, n, k, s));
+  return gemm_impl(tq2::Fmt::kTq2, m <= 1 ? 0 : 1, soa, x, residual, out, m, n, k, stream);
 }
 
 int tq2_gate_up_swiglu(const void* gate_soa, const void* up_soa, const float* x, float* out,
                        int64_t m, int64_t n, int64_t k, void* stream) {
-  int st = check_shape(m, n, k);
+  return swiglu_impl(tq2::Fmt::kTq2, gate_soa, up_soa, x, out, m, n, k, stream);
+}
+
+size_t tq2_q1_aos_bytes(int64_t n, int64_t k) {
+  if (check_shape(0, n, k) != TQ2_OK) return 0;
+  return size_t(n) * size_t(k / tq2::kBlockWeights) * tq2::kQ1BlockBytes;
+}
+
+size_t tq2_q1_soa_bytes(int64_t n, int64_t k) {
+  if (check_shape(0, n, k) != TQ2_OK) return 0;
+  return tq2::soa_bytes(tq2::Fmt::kQ1, n, k);
+}
+
+int tq2_q1_reformat_aos_to_soa(const void* aos, void* soa, int64_t n, int64_t k, void* stream) {
+  return reformat_impl(tq2::Fmt::kQ1, aos, soa, n, k, stream);
+}
+
+int tq2_q1_gemv(const void* soa, const float* x, const float* residual, float* out, int64_t n,
+                int64_t k, void* stream) {
+  return gemv_impl(tq2::Fmt::kQ1, soa, x, residual, out, n, k, stream);
+}
+
+int tq2_q1_gemm(const void* soa, const float* x, const float* residual, float* out, int64_t m,
+                int64_t n, int64_t k, void* stream) {
+  const int st = check_shape(m, n, k);
   if (st != TQ2_OK) return st;
   if (m == 0 || n == 0) return TQ2_OK;
-  if (!up_soa) return TQ2_ERR_INVALID;
-  st = check_matmul_host(gate_soa, x, nullptr, out, m, n, k);
-  if (st != TQ2_OK) return st;
-  if (!aligned(up_soa, 256)) return TQ2_ERR_ALIGN;
-  if (overlaps(out, size_t(m) * size_t(n) * 4, up_soa, tq2::soa_bytes(n, k)))
-    return TQ2_ERR_ALIAS;
-  const int path = tq2_gemm_path(m, n, k);
-  if (path != 0 && (k > tq2::kGemmMaxK || n * (k / 4) >= tq2::kGemmMaxCodeBytes))
-    return TQ2_ERR_INVALID;
-  st = check_device();
-  if (st != TQ2_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint8_t* g = static_cast<const uint8_t*>(gate_soa);
-  const uint8_t* u = static_cast<const uint8_t*>(up_soa);
-  if (path == 0) return launch_status(tq2::launch_gemv_swiglu(g, u, x, out, n, k, s));
-  return launch_status(tq2::launch_gemm_swiglu(path, g, u, x, out, m, n, k, s));
+  return gemm_impl(tq2::Fmt::kQ1, tq2_gemm_path(m, n, k), soa, x, residual, out, m, n, k, stream);
+}
+
+int tq2_q1_gate_up_swiglu(const void* gate_soa, const void* up_soa, const float* x, float* out,
+                          int64_t m, int64_t n, int64_t k, void* stream) {
+  return swiglu_impl(tq2::Fmt::kQ1, gate_soa, up_soa, x, out, m, n, k, stream);
 }
 
 const char* tq2_status_string(int status) {

@@ -27,6 +27,12 @@
 //    other half the same columns of the up weight, on the same x tile; the
 //    epilogue meets each pair in LDS and stores silu(g) * u, silu(z) =
 //    z / (1 + e^-z).  Neither projection goes to memory.
+//  * F = Fmt::kQ1 runs the same kernels on Q1_g128 (1-bit) weights (the
+//    pages' `gemm_q1_g128_v7` / `_residual` / `fused_gate_up_swiglu_gemm_q1`):
+//    a lane's word holds four steps' bits; shifting a pair's two bits onto
+//    the binary16 sign positions and OR-ing |d| gives the exact pair
+//    (+-|d|, +-|d|) in two instructions (the word is complemented once per
+//    chunk when d > 0, so the sign bit marks the negative weights).
 //  * Blocks are numbered so that the N-tiles of the same M rows land on the
 //    same XCD (the dispatcher deals block ids round-robin over 8 XCDs): x, at
 //    4 bytes per element, is the costly operand to re-fetch, so an XCD's L2
@@ -87,6 +93,28 @@ __device__ __forceinline__ half8_t decode_step(uint32_t word, half2_t d2, uint32
   return b;
 }
 
+// Q1: four binary16 pairs (8 weights) of one MFMA step.  Pair p = base + r
+// of `word` has its bits at p and p + 16; shifting left by 15 - p puts them
+// on the two sign bits and the AND-OR adds the magnitude pair `dabs2`
+// (|d|, |d|).  `word` is complemented beforehand when d is positive, so a set
+// sign bit is exactly a negative weight: the pair is ((2b-1) d, (2b'-1) d).
+__device__ __forceinline__ half8_t decode_step_q1(uint32_t word, int base, uint32_t dabs2) {
+  half8_t b;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p = base + r;
+    const half2_t val = as_half2(and_or(word << (15 - p), 0x80008000u, dabs2));
+    b[2 * r] = val[0];
+    b[2 * r + 1] = val[1];
+  }
+  return b;
+}
+
+// Q1 decode operands of one block scale: the |d| pair and the word mask that
+// complements the bits when d is positive (sign bit clear).
+__device__ __forceinline__ uint32_t q1_dabs2(uint32_t dbits) { return (dbits & 0x7FFFu) * 0x10001u; }
+__device__ __forceinline__ uint32_t q1_fold(uint32_t dbits) { return ((dbits >> 15) & 1u) - 1u; }
+
 // Wait for this wave's LDS accesses, then join the workgroup barrier.  The
 // asm's memory clobber keeps the compiler from moving memory accesses across
 // it; unlike __syncthreads() it leaves the wave's global loads in flight.
@@ -116,7 +144,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 // waves wn < WN/2 read the gate weight (codes, scales) and the others the
 // same columns of the up weight (ucodes, uscales): the output tile is
 // MT x (WN/2 * NW).
-template <int MT, int NW, int WN, int WK, int LIMBS, bool SWIGLU>
+template <int MT, int NW, int WN, int WK, int LIMBS, bool SWIGLU, Fmt F>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
@@ -127,7 +155,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
   constexpr int CG = NW / 16;            // 16-column groups per wave
   constexpr int NT = SWIGLU ? WN / 2 * NW : WN * NW;   // output columns per block
   constexpr int STEPS = 8 / WK;          // MFMA k-steps per wave per chunk
-  constexpr int QW = 4 / WK;             // code dwords per lane per chunk
+  constexpr int BITS = int(F);           // code bits per weight
+  constexpr int QW = BITS * 2 / WK;      // code dwords per lane per chunk
   constexpr int AV = MT * (kChunk / 4) / THREADS;   // float4 A loads per thread per chunk
   static_assert(MT % 16 == 0 && NW % 16 == 0, "tile shape");
   static_assert(WK == 1 || WK == 2, "k split");
@@ -162,7 +191,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
 
   // x rows m0 .. m0+MT-1 (rows past M read as zero).
   const rsrc_t rx = make_rsrc(x + size_t(m0) * K, uint32_t(min(MT, M - m0)) * uint32_t(K) * 4u);
-  const rsrc_t rc = make_rsrc(upw ? ucodes : codes, uint32_t(N) * uint32_t(K / 4));
+  const uint32_t row_bytes = uint32_t(K / 8) * uint32_t(BITS);   // codes per weight row
+  const rsrc_t rc = make_rsrc(upw ? ucodes : codes, uint32_t(N) * row_bytes);
   const rsrc_t rs = make_rsrc(upw ? uscales : scales, uint32_t(N) * uint32_t(KB) * 2u);
 
   // Per-thread byte offsets, fixed for the whole K loop; a chunk, an A row
@@ -201,19 +231,20 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
   // the raw binary16 scale of the block they fall in.  Columns past N read as
   // zero codes and zero scales.
   const uint32_t nl = uint32_t(n0 + wc * NW + col);
-  const uint32_t code_voff = nl * uint32_t(K / 4) + 16u * uint32_t(g) + 4u * QW * uint32_t(wk);
+  const uint32_t code_voff = nl * row_bytes + 8u * BITS * uint32_t(g) + 4u * QW * uint32_t(wk);
   const uint32_t scale_voff = (nl * uint32_t(KB) + uint32_t(g >> 1)) * 2u;
   auto load_w = [&](int c, codes_t (&cw)[CG], _Float16 (&dsc)[CG]) {
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
+      const uint32_t off = code_voff + uint32_t(j * 16) * row_bytes + uint32_t(c * 32 * BITS);
       if constexpr (QW == 4) {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
-            rc, code_voff + uint32_t(j * 16 * (K / 4) + c * 64), 0, 0);
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
         cw[j][0] = v[0]; cw[j][1] = v[1]; cw[j][2] = v[2]; cw[j][3] = v[3];
-      } else {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(
-            rc, code_voff + uint32_t(j * 16 * (K / 4) + c * 64), 0, 0);
+      } else if constexpr (QW == 2) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
         cw[j][0] = v[0]; cw[j][1] = v[1];
+      } else {
+        cw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0);
       }
       dsc[j] = __builtin_bit_cast(
           _Float16, __builtin_amdgcn_raw_buffer_load_b16(
@@ -237,13 +268,19 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
       for (int l = 0; l < LIMBS; ++l)
         a[i][l] = *reinterpret_cast<const half8_t*>(&As[buf][l][i * 16 + col][64 * g + 8 * s]);
   };
+  // TQ2: d2 is the pair (d, d) and cw the raw words.  Q1: d2 holds the bits
+  // of (|d|, |d|) and cw the words after the sign fold.
   auto decode_bfrags = [&](int ss, const codes_t (&cw)[CG], const half2_t (&d2)[CG],
                            half8_t (&b)[CG]) {
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      uint32_t w = cw[j][ss >> 1];
-      if (ss & 1) w >>= 8;
-      b[j] = decode_step(w, d2[j], magic);
+      if constexpr (F == Fmt::kQ1) {
+        b[j] = decode_step_q1(cw[j][ss >> 2], 4 * (ss & 3), __builtin_bit_cast(uint32_t, d2[j]));
+      } else {
+        uint32_t w = cw[j][ss >> 1];
+        if (ss & 1) w >>= 8;
+        b[j] = decode_step(w, d2[j], magic);
+      }
     }
   };
   auto mfmas = [&](const half8_t (&a)[RT][LIMBS], const half8_t (&b)[CG]) {
@@ -270,15 +307,28 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
     }
   };
 
-  auto compute = [&](int c, int buf, const codes_t (&cw)[CG], const _Float16 (&dsc)[CG]) {
-    // binary16 pair (d, d), or (0, 0) where k runs past K in the last chunk.
+  auto compute = [&](int c, int buf, const codes_t (&cw_raw)[CG], const _Float16 (&dsc)[CG]) {
+    // binary16 pair (d, d), or (0, 0) where k runs past K in the last chunk
+    // (Q1: the |d| pair, and the words folded by the sign of d).
     const bool live = c * kChunk + 64 * g < K;
     half2_t dw[CG];
+    codes_t cf[CG];
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
       const _Float16 d = live ? dsc[j] : _Float16(0.0f);
-      dw[j] = half2_t{d, d};
+      if constexpr (F == Fmt::kQ1) {
+        const uint32_t db = __builtin_bit_cast(uint16_t, d);
+        dw[j] = __builtin_bit_cast(half2_t, q1_dabs2(db));
+        const uint32_t fold = q1_fold(db);
+#pragma unroll
+        for (int q = 0; q < QW; ++q) cf[j][q] = cw_raw[j][q] ^ fold;
+      } else {
+        dw[j] = half2_t{d, d};
+#pragma unroll
+        for (int q = 0; q < QW; ++q) cf[j][q] = cw_raw[j][q];
+      }
     }
+    const codes_t (&cw)[CG] = cf;
     half8_t a0[RT][LIMBS], a1[RT][LIMBS], b0[CG], b1[CG];
     load_afrags(buf, wk * STEPS, a0);
     decode_bfrags(0, cw, dw, b0);
@@ -444,7 +494,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
 //
 // SWIGLU: waves wn = 0, 1 of each group read gate-weight columns, waves 2, 3
 // the same columns of the up weight; the output tile is MT x 2NW.
-template <int MT, int NW, bool SWIGLU>
+template <int MT, int NW, bool SWIGLU, Fmt F>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
@@ -456,7 +506,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   constexpr int NT = 4 * NW;             // weight rows per block
   constexpr int NO = SWIGLU ? 2 * NW : NT;   // output columns per block
   constexpr int STEPS = 4;               // MFMA steps per group per chunk
-  constexpr int QW = 2;                  // code dwords per lane per chunk
+  constexpr int BITS = int(F);           // code bits per weight
+  constexpr int QW = BITS;               // code dwords per lane per chunk
   constexpr int AV = MT * (kChunk / 4) / 2 / GT;   // float4 of x per thread per chunk
   static_assert(MT % 32 == 0 && NW % 16 == 0, "tile shape");
   static_assert((MT / 2) * (kChunk / 4) % GT == 0, "x staging split");
@@ -490,7 +541,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   const int nchunks = (K + kChunk - 1) / kChunk;
 
   const rsrc_t rx = make_rsrc(x + size_t(m0) * K, uint32_t(min(MT, M - m0)) * uint32_t(K) * 4u);
-  const rsrc_t rc = make_rsrc(upw ? ucodes : codes, uint32_t(N) * uint32_t(K / 4));
+  const uint32_t row_bytes = uint32_t(K / 8) * uint32_t(BITS);   // codes per weight row
+  const rsrc_t rc = make_rsrc(upw ? ucodes : codes, uint32_t(N) * row_bytes);
 
   // x staging: group p converts rows p*MT/2 .. p*MT/2 + MT/2 - 1 of a chunk;
   // its thread gt handles float4 f = gt + GT*i: row f / 64, float4 f % 64.
@@ -518,15 +570,19 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
 
   // Weights: lane's column, its k-group g, this group's half of the steps.
   const uint32_t nl = uint32_t(n0 + wc * NW + col);
-  const uint32_t code_voff = nl * uint32_t(K / 4) + 16u * uint32_t(g) + 4u * QW * uint32_t(grp);
+  const uint32_t code_voff = nl * row_bytes + 8u * BITS * uint32_t(g) + 4u * QW * uint32_t(grp);
   uint32_t cw[CG][QW];
   auto load_w = [&](int c) {
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(
-            rc, code_voff + uint32_t(j * 16 * (K / 4) + c * 64), 0, 0);
-      cw[j][0] = v[0];
-      cw[j][1] = v[1];
+      const uint32_t off = code_voff + uint32_t(j * 16) * row_bytes + uint32_t(c * 32 * BITS);
+      if constexpr (QW == 2) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
+        cw[j][0] = v[0];
+        cw[j][1] = v[1];
+      } else {
+        cw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0);
+      }
     }
   };
   // Scale of this lane's column j and chunk c: block 2c + (g >> 1).  The
@@ -552,15 +608,26 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
       const _Float16 d = live ? scale_of(j, c) : _Float16(0.0f);
-      const half2_t d2 = {d, d};
+      if constexpr (F == Fmt::kQ1) {
+        // One word holds the four steps; dlast carries the |d| pair's bits.
+        const uint32_t db = __builtin_bit_cast(uint16_t, d);
+        const uint32_t da = q1_dabs2(db);
+        const uint32_t w = cw[j][0] ^ q1_fold(db);
 #pragma unroll
-      for (int ss = 0; ss < STEPS - 1; ++ss) {
-        uint32_t w = cw[j][ss >> 1];
-        if (ss & 1) w >>= 8;
-        bf[ss][j] = decode_step(w, d2, magic);
+        for (int ss = 0; ss < STEPS - 1; ++ss) bf[ss][j] = decode_step_q1(w, 4 * ss, da);
+        wlast[j] = w;
+        dlast[j] = __builtin_bit_cast(half2_t, da);
+      } else {
+        const half2_t d2 = {d, d};
+#pragma unroll
+        for (int ss = 0; ss < STEPS - 1; ++ss) {
+          uint32_t w = cw[j][ss >> 1];
+          if (ss & 1) w >>= 8;
+          bf[ss][j] = decode_step(w, d2, magic);
+        }
+        wlast[j] = cw[j][(STEPS - 1) >> 1] >> 8;
+        dlast[j] = d2;
       }
-      wlast[j] = cw[j][(STEPS - 1) >> 1] >> 8;
-      dlast[j] = d2;
     }
   };
 
@@ -606,7 +673,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
       // Last step's operands, one column group per earlier step.
 #pragma unroll
       for (int j = 0; j < CG; ++j)
-        if (ss == (j * (STEPS - 1)) / CG) bf[STEPS - 1][j] = decode_step(wlast[j], dlast[j], magic);
+        if (ss == (j * (STEPS - 1)) / CG) {
+          if constexpr (F == Fmt::kQ1)
+            bf[STEPS - 1][j] = decode_step_q1(wlast[j], 4 * (STEPS - 1),
+                                              __builtin_bit_cast(uint32_t, dlast[j]));
+          else
+            bf[STEPS - 1][j] = decode_step(wlast[j], dlast[j], magic);
+        }
 #pragma unroll
       for (int q = 0; q < RT * CG; ++q) {
         if (q % CG == 0 && ss + 1 < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -777,7 +850,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
 }
 
 // `up` is null for the plain matmul; with SWIGLU, `soa` is the gate weight.
-template <int MT, int NW, bool SWIGLU>
+template <int MT, int NW, bool SWIGLU, Fmt F>
 hipError_t launch_pp(const uint8_t* soa, const uint8_t* up, const float* x,
                      const float* residual, float* out, int64_t m, int64_t n, int64_t k,
                      hipStream_t stream) {
@@ -786,14 +859,14 @@ hipError_t launch_pp(const uint8_t* soa, const uint8_t* up, const float* x,
   const int64_t tn = (n + NO - 1) / NO;
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(unsigned(tm * tn));
-  const size_t so = scales_offset(n, k);
-  hipLaunchKernelGGL((gemm_pp_kernel<MT, NW, SWIGLU>), grid, dim3(512), 0, stream, soa, soa + so,
+  const size_t so = scales_offset(F, n, k);
+  hipLaunchKernelGGL((gemm_pp_kernel<MT, NW, SWIGLU, F>), grid, dim3(512), 0, stream, soa, soa + so,
                      up, up ? up + so : nullptr, x, residual, out, int(m), int(n), int(k), int(tm),
                      int(tn));
   return hipGetLastError();
 }
 
-template <int MT, int NW, int WN, int WK, int LIMBS, bool SWIGLU>
+template <int MT, int NW, int WN, int WK, int LIMBS, bool SWIGLU, Fmt F>
 hipError_t launch_tile(const uint8_t* soa, const uint8_t* up, const float* x,
                        const float* residual, float* out, int64_t m, int64_t n, int64_t k,
                        hipStream_t stream) {
@@ -803,15 +876,15 @@ hipError_t launch_tile(const uint8_t* soa, const uint8_t* up, const float* x,
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int tiles_m = int(tm), tiles_n = int(tn);
   const dim3 grid(unsigned(tm * tn));
-  const size_t so = scales_offset(n, k);
-  hipLaunchKernelGGL((gemm_kernel<MT, NW, WN, WK, LIMBS, SWIGLU>), grid, dim3(64 * WN * WK), 0,
+  const size_t so = scales_offset(F, n, k);
+  hipLaunchKernelGGL((gemm_kernel<MT, NW, WN, WK, LIMBS, SWIGLU, F>), grid, dim3(64 * WN * WK), 0,
                      stream, soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m),
                      int(n), int(k), tiles_m, tiles_n);
   return hipGetLastError();
 }
 
 // Kernel choice by path and M (shared by the plain and the SwiGLU forms).
-template <bool SWIGLU>
+template <bool SWIGLU, Fmt F>
 hipError_t dispatch(int path, const uint8_t* soa, const uint8_t* up, const float* x,
                     const float* residual, float* out, int64_t m, int64_t n, int64_t k,
                     hipStream_t stream) {
@@ -820,30 +893,41 @@ hipError_t dispatch(int path, const uint8_t* soa, const uint8_t* up, const float
     // tiles beyond (tq2_gemm_precise), so each weight is decoded once per 64
     // rows of x.
     if (m <= 16)
-      return launch_tile<16, 16, 4, 2, 2, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
-    return launch_tile<64, 16, 4, 2, 2, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+      return launch_tile<16, 16, 4, 2, 2, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+    return launch_tile<64, 16, 4, 2, 2, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
   }
   if (m <= 32)
-    return launch_tile<32, 16, 4, 2, 1, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+    return launch_tile<32, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
   if (m <= 64)
-    return launch_tile<64, 16, 4, 2, 1, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+    return launch_tile<64, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
   if (m <= 128)
-    return launch_tile<128, 16, 4, 2, 1, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+    return launch_tile<128, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
   if (k <= int64_t(kPpMaxKB) * kBlockWeights)
-    return launch_pp<96, 48, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
-  return launch_tile<96, 48, 4, 2, 1, SWIGLU>(soa, up, x, residual, out, m, n, k, stream);
+    return launch_pp<96, 48, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+  return launch_tile<96, 48, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int path, const uint8_t* soa, const float* x, const float* residual,
                        float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  return dispatch<false>(path, soa, nullptr, x, residual, out, m, n, k, stream);
+  return dispatch<false, Fmt::kTq2>(path, soa, nullptr, x, residual, out, m, n, k, stream);
 }
 
 hipError_t launch_gemm_swiglu(int path, const uint8_t* gate, const uint8_t* up, const float* x,
                               float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
-  return dispatch<true>(path, gate, up, x, nullptr, out, m, n, k, stream);
+  return dispatch<true, Fmt::kTq2>(path, gate, up, x, nullptr, out, m, n, k, stream);
+}
+
+hipError_t launch_gemm_q1(int path, const uint8_t* soa, const float* x, const float* residual,
+                          float* out, int64_t m, int64_t n, int64_t k, hipStream_t stream) {
+  return dispatch<false, Fmt::kQ1>(path, soa, nullptr, x, residual, out, m, n, k, stream);
+}
+
+hipError_t launch_gemm_swiglu_q1(int path, const uint8_t* gate, const uint8_t* up,
+                                 const float* x, float* out, int64_t m, int64_t n, int64_t k,
+                                 hipStream_t stream) {
+  return dispatch<true, Fmt::kQ1>(path, gate, up, x, nullptr, out, m, n, k, stream);
 }
 
 }  // namespace tq2

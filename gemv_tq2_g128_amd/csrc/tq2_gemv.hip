@@ -23,6 +23,12 @@
 // v_fma_mix_f32 (f32 x times binary16 weight, f32 accumulate).  Each lane's
 // 16-term sum is scaled by its block's d once; the partial sums of a row are
 // added in LDS and with cross-lane shuffles, and the residual is added last.
+//
+// Q1_g128 weights (the pages' `gemv_q1_g128_v7` / `_residual` decode kernels,
+// same table) run the same kernels with F = Fmt::kQ1: a lane's word holds 32
+// weights, each pair's two bits are shifted onto the binary16 sign positions
+// and OR-ed with 1.0, giving the exact pair ((-1)^b, (-1)^b'), and the 32-term
+// sum is scaled by -d.
 #include "tq2_internal.h"
 
 namespace tq2 {
@@ -57,6 +63,10 @@ __device__ __forceinline__ void decode_word(uint32_t w, uint32_t magic, half2_t 
   }
 }
 
+// Weights per 32-bit code word of the SoA codes plane.
+template <Fmt F>
+constexpr int kWpw = F == Fmt::kQ1 ? 32 : 16;
+
 __device__ __forceinline__ float dot16(const half2_t (&v)[8], const float (&xv)[16]) {
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -67,13 +77,27 @@ __device__ __forceinline__ float dot16(const half2_t (&v)[8], const float (&xv)[
   return s0 + s1;
 }
 
-// Load ROWS code words and scales of word wc, and the 16 x values of it.
-template <int ROWS>
+// Sum of x[t] * (2 b_t - 1) over the 32 weights of one Q1 word (exact +-1
+// pairs, f32 products and sums).
+__device__ __forceinline__ float dot32_q1(uint32_t w, const float (&xv)[32]) {
+  const uint32_t one = 0x3C003C00u;             // binary16 pair (1, 1)
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const half2_t v = __builtin_bit_cast(half2_t, and_or(w << (15 - p), 0x80008000u, one));
+    s0 = __builtin_fmaf(xv[2 * p], float(v[0]), s0);
+    s1 = __builtin_fmaf(xv[2 * p + 1], float(v[1]), s1);
+  }
+  return -(s0 + s1);                            // (-1)^b = -(2b - 1)
+}
+
+// Load ROWS code words and scales of word wc, and the kWpw x values of it.
+template <int ROWS, Fmt F>
 __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
                                              const uint16_t* __restrict__ scales,
                                              const float* __restrict__ x, int row0, int n_rows,
                                              int wpr, int kb_count, int wc, uint32_t (&cw)[ROWS],
-                                             uint32_t (&db)[ROWS], float (&xv)[16]) {
+                                             uint32_t (&db)[ROWS], float (&xv)[kWpw<F>]) {
   const unsigned uwc = unsigned(wc);            // lane offset: 32-bit, base pointer uniform
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
@@ -81,11 +105,11 @@ __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
     const uint32_t* crow = codes + size_t(row) * wpr;
     const uint16_t* srow = scales + size_t(row) * kb_count;
     cw[r] = crow[uwc];
-    db[r] = srow[uwc >> 3];
+    db[r] = srow[uwc / (kBlockWeights / kWpw<F>)];
   }
-  const float4* xp = reinterpret_cast<const float4*>(x + 16 * wc);
+  const float4* xp = reinterpret_cast<const float4*>(x + kWpw<F> * wc);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kWpw<F> / 4; ++i) {
     const float4 q = xp[i];
     xv[4 * i] = q.x;
     xv[4 * i + 1] = q.y;
@@ -94,18 +118,23 @@ __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
   }
 }
 
-template <int ROWS>
+template <int ROWS, Fmt F>
 __device__ __forceinline__ void accumulate_segment(const uint32_t (&cw)[ROWS],
                                                    const uint32_t (&db)[ROWS],
-                                                   const float (&xv)[16], bool live,
+                                                   const float (&xv)[kWpw<F>], bool live,
                                                    float (&part)[ROWS]) {
   const uint32_t magic = kMagic;
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    half2_t v[8];
-    decode_word(cw[r], magic, v);
     const float d = float(__builtin_bit_cast(_Float16, uint16_t(db[r])));
-    const float s = dot16(v, xv) * d;
+    float s;
+    if constexpr (F == Fmt::kQ1) {
+      s = dot32_q1(cw[r], xv) * d;
+    } else {
+      half2_t v[8];
+      decode_word(cw[r], magic, v);
+      s = dot16(v, xv) * d;
+    }
     part[r] += live ? s : 0.f;
   }
 }
@@ -113,7 +142,7 @@ __device__ __forceinline__ void accumulate_segment(const uint32_t (&cw)[ROWS],
 // One block's rows: block `blk` covers rows blk * OUTS .. blk * OUTS + OUTS - 1
 // of an [n_rows, k] weight.  ONE_SEG: K/16 <= LPS, the whole row fits one
 // pass and every load of the thread is issued before the first use.
-template <int ROWS, int LPS, bool ONE_SEG>
+template <int ROWS, int LPS, bool ONE_SEG, Fmt F = Fmt::kTq2>
 __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
                                            const uint16_t* __restrict__ scales,
                                            const float* __restrict__ x,
@@ -127,7 +156,7 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
   // With one slot per block the row indices are block-uniform (scalar).
   const int slot = SLOTS == 1 ? 0 : t / LPS;
   const int lw = SLOTS == 1 ? t : t % LPS;      // word index inside a K segment
-  const int wpr = k >> 4;                       // code words per row
+  const int wpr = k / kWpw<F>;                  // code words per row
   const int kb_count = k >> 7;
   const int row0 = blk * OUTS + slot * ROWS;
 
@@ -137,24 +166,24 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
 
   uint32_t cw[ROWS];
   uint32_t db[ROWS];
-  float xv[16];
+  float xv[kWpw<F>];
   if constexpr (ONE_SEG) {
     if (wpr == LPS) {                           // every lane has a word: no masking
-      load_segment<ROWS>(codes, scales, x, row0, n_rows, wpr, kb_count, lw, cw, db, xv);
-      accumulate_segment<ROWS>(cw, db, xv, true, part);
+      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, wpr, kb_count, lw, cw, db, xv);
+      accumulate_segment<ROWS, F>(cw, db, xv, true, part);
     } else {
       const bool live = lw < wpr;
-      load_segment<ROWS>(codes, scales, x, row0, n_rows, wpr, kb_count, live ? lw : wpr - 1,
-                         cw, db, xv);
-      accumulate_segment<ROWS>(cw, db, xv, live, part);
+      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, wpr, kb_count, live ? lw : wpr - 1,
+                            cw, db, xv);
+      accumulate_segment<ROWS, F>(cw, db, xv, live, part);
     }
   } else {
     for (int seg = 0; seg < wpr; seg += LPS) {
       const int w = seg + lw;
       const bool live = w < wpr;
-      load_segment<ROWS>(codes, scales, x, row0, n_rows, wpr, kb_count, live ? w : wpr - 1, cw,
-                         db, xv);
-      accumulate_segment<ROWS>(cw, db, xv, live, part);
+      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, wpr, kb_count, live ? w : wpr - 1,
+                            cw, db, xv);
+      accumulate_segment<ROWS, F>(cw, db, xv, live, part);
     }
   }
 
@@ -182,14 +211,14 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
   }
 }
 
-template <int ROWS, int LPS, bool ONE_SEG>
+template <int ROWS, int LPS, bool ONE_SEG, Fmt F>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const uint32_t* __restrict__ codes,
                                                         const uint16_t* __restrict__ scales,
                                                         const float* __restrict__ x,
                                                         const float* __restrict__ residual,
                                                         float* __restrict__ out, int n_rows,
                                                         int k) {
-  gemv_block<ROWS, LPS, ONE_SEG>(codes, scales, x, residual, out, n_rows, k, blockIdx.x);
+  gemv_block<ROWS, LPS, ONE_SEG, F>(codes, scales, x, residual, out, n_rows, k, blockIdx.x);
 }
 
 // Several independent GEMVs with the same k in one launch: block b belongs to
@@ -224,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void gemv_batched_kernel(const GemvBatchA
 // holds g[n] and u[n] together.  Neither projection leaves the chip.
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-template <int LPS, bool ONE_SEG>
+template <int LPS, bool ONE_SEG, Fmt F>
 __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
     const uint32_t* __restrict__ gcodes, const uint16_t* __restrict__ gscales,
     const uint32_t* __restrict__ ucodes, const uint16_t* __restrict__ uscales,
@@ -238,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   const int t = threadIdx.x;
   const int slot = SLOTS == 1 ? 0 : t / LPS;
   const int lw = SLOTS == 1 ? t : t % LPS;
-  const int wpr = k >> 4;
+  const int wpr = k / kWpw<F>;
   const int kb_count = k >> 7;
   const int out0 = blockIdx.x * OUTS + slot * HALF;
 
@@ -247,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   for (int r = 0; r < ROWS; ++r) part[r] = 0.f;
   uint32_t cw[ROWS];
   uint32_t db[ROWS];
-  float xv[16];
+  float xv[kWpw<F>];
   // Rows 0..HALF-1 from the gate weight, HALF..ROWS-1 from the up weight.
   auto load = [&](int wc) {
     const unsigned uwc = unsigned(wc);
@@ -257,11 +286,11 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
       const uint32_t* crow = (r < HALF ? gcodes : ucodes) + size_t(row) * wpr;
       const uint16_t* srow = (r < HALF ? gscales : uscales) + size_t(row) * kb_count;
       cw[r] = crow[uwc];
-      db[r] = srow[uwc >> 3];
+      db[r] = srow[uwc / (kBlockWeights / kWpw<F>)];
     }
-    const float4* xp = reinterpret_cast<const float4*>(x + 16 * wc);
+    const float4* xp = reinterpret_cast<const float4*>(x + kWpw<F> * wc);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kWpw<F> / 4; ++i) {
       const float4 q = xp[i];
       xv[4 * i] = q.x;
       xv[4 * i + 1] = q.y;
@@ -272,13 +301,13 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   if constexpr (ONE_SEG) {
     const bool live = lw < wpr;
     load(live ? lw : wpr - 1);
-    accumulate_segment<ROWS>(cw, db, xv, live, part);
+    accumulate_segment<ROWS, F>(cw, db, xv, live, part);
   } else {
     for (int seg = 0; seg < wpr; seg += LPS) {
       const int w = seg + lw;
       const bool live = w < wpr;
       load(live ? w : wpr - 1);
-      accumulate_segment<ROWS>(cw, db, xv, live, part);
+      accumulate_segment<ROWS, F>(cw, db, xv, live, part);
     }
   }
 
@@ -306,15 +335,15 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   if (g == 0 && row < n_rows) out[row] = silu(vg) * vu;
 }
 
-template <int ROWS>
+template <int ROWS, Fmt F>
 hipError_t launch_rows(int lps, const uint32_t* codes, const uint16_t* scales, const float* x,
                        const float* residual, float* out, int n, int k, hipStream_t stream) {
   const int outs = (kThreads / lps) * ROWS;
   const dim3 grid((n + outs - 1) / outs);
 #define TQ2_GEMV_CASE(L)                                                                     \
   case L:                                                                                    \
-    hipLaunchKernelGGL((gemv_kernel<ROWS, L, true>), grid, dim3(kThreads), 0, stream, codes,   \
-                       scales, x, residual, out, n, k);                                      \
+    hipLaunchKernelGGL((gemv_kernel<ROWS, L, true, F>), grid, dim3(kThreads), 0, stream,      \
+                       codes, scales, x, residual, out, n, k);                               \
     break;
   switch (lps) {
     TQ2_GEMV_CASE(8)
@@ -323,11 +352,11 @@ hipError_t launch_rows(int lps, const uint32_t* codes, const uint16_t* scales, c
     TQ2_GEMV_CASE(64)
     TQ2_GEMV_CASE(128)
     default:
-      if (k / 16 <= 256)
-        hipLaunchKernelGGL((gemv_kernel<ROWS, 256, true>), grid, dim3(kThreads), 0, stream, codes,
-                           scales, x, residual, out, n, k);
+      if (k / kWpw<F> <= 256)
+        hipLaunchKernelGGL((gemv_kernel<ROWS, 256, true, F>), grid, dim3(kThreads), 0, stream,
+                           codes, scales, x, residual, out, n, k);
       else
-        hipLaunchKernelGGL((gemv_kernel<ROWS, 256, false>), grid, dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((gemv_kernel<ROWS, 256, false, F>), grid, dim3(kThreads), 0, stream,
                            codes, scales, x, residual, out, n, k);
       break;
   }
@@ -363,9 +392,9 @@ hipError_t launch_batched_rows(int lps, const GemvBatchArgs& args, int blocks, i
   return hipGetLastError();
 }
 
-// Lanes per row slot for a given k: a power of two >= k/16, at most 256.
-int lanes_per_slot(int64_t k) {
-  const int64_t wpr = k / 16;
+// Lanes per row slot for a given k: a power of two >= k/kWpw, at most 256.
+int lanes_per_slot(int64_t k, Fmt f = Fmt::kTq2) {
+  const int64_t wpr = k / (f == Fmt::kQ1 ? 32 : 16);
   int lps = 8;
   while (lps < wpr && lps < kThreads) lps <<= 1;
   return lps;
@@ -373,13 +402,16 @@ int lanes_per_slot(int64_t k) {
 
 }  // namespace
 
-hipError_t launch_gemv_swiglu(const uint8_t* gate, const uint8_t* up, const float* x,
-                              float* out, int64_t n, int64_t k, hipStream_t stream) {
+namespace {
+
+template <Fmt F>
+hipError_t launch_swiglu_fmt(const uint8_t* gate, const uint8_t* up, const float* x, float* out,
+                             int64_t n, int64_t k, hipStream_t stream) {
   const uint32_t* gc = reinterpret_cast<const uint32_t*>(gate);
-  const uint16_t* gs = reinterpret_cast<const uint16_t*>(gate + scales_offset(n, k));
+  const uint16_t* gs = reinterpret_cast<const uint16_t*>(gate + scales_offset(F, n, k));
   const uint32_t* uc = reinterpret_cast<const uint32_t*>(up);
-  const uint16_t* us = reinterpret_cast<const uint16_t*>(up + scales_offset(n, k));
-  const int lps = lanes_per_slot(k);
+  const uint16_t* us = reinterpret_cast<const uint16_t*>(up + scales_offset(F, n, k));
+  const int lps = lanes_per_slot(k, F);
   const int outs = (kThreads / lps) * 4;
   const int64_t blocks = (n + outs - 1) / outs;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -387,8 +419,8 @@ hipError_t launch_gemv_swiglu(const uint8_t* gate, const uint8_t* up, const floa
   const int ni = int(n), ki = int(k);
 #define TQ2_SWIGLU_CASE(L)                                                                    \
   case L:                                                                                     \
-    hipLaunchKernelGGL((gemv_swiglu_kernel<L, true>), grid, dim3(kThreads), 0, stream, gc, gs, \
-                       uc, us, x, out, ni, ki);                                               \
+    hipLaunchKernelGGL((gemv_swiglu_kernel<L, true, F>), grid, dim3(kThreads), 0, stream, gc,  \
+                       gs, uc, us, x, out, ni, ki);                                           \
     break;
   switch (lps) {
     TQ2_SWIGLU_CASE(8)
@@ -397,16 +429,44 @@ hipError_t launch_gemv_swiglu(const uint8_t* gate, const uint8_t* up, const floa
     TQ2_SWIGLU_CASE(64)
     TQ2_SWIGLU_CASE(128)
     default:
-      if (k / 16 <= 256)
-        hipLaunchKernelGGL((gemv_swiglu_kernel<256, true>), grid, dim3(kThreads), 0, stream, gc,
-                           gs, uc, us, x, out, ni, ki);
+      if (k / kWpw<F> <= 256)
+        hipLaunchKernelGGL((gemv_swiglu_kernel<256, true, F>), grid, dim3(kThreads), 0, stream,
+                           gc, gs, uc, us, x, out, ni, ki);
       else
-        hipLaunchKernelGGL((gemv_swiglu_kernel<256, false>), grid, dim3(kThreads), 0, stream, gc,
-                           gs, uc, us, x, out, ni, ki);
+        hipLaunchKernelGGL((gemv_swiglu_kernel<256, false, F>), grid, dim3(kThreads), 0, stream,
+                           gc, gs, uc, us, x, out, ni, ki);
       break;
   }
 #undef TQ2_SWIGLU_CASE
   return hipGetLastError();
+}
+
+template <Fmt F>
+hipError_t launch_gemv_fmt(const uint8_t* soa, const float* x, const float* residual, float* out,
+                           int64_t n, int64_t k, hipStream_t stream) {
+  const uint32_t* codes = reinterpret_cast<const uint32_t*>(soa);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(soa + scales_offset(F, n, k));
+  const int lps = lanes_per_slot(k, F);
+  // Rows per thread: 8 when that still gives >= 2 blocks per CU, else fewer.
+  const int slots = kThreads / lps;
+  int rows = 8;
+  while (rows > 4 && (n + int64_t(slots) * rows - 1) / (int64_t(slots) * rows) < 512) rows >>= 1;
+  if (rows > lps) rows = lps;
+  const int ni = int(n), ki = int(k);
+  if (rows == 8) return launch_rows<8, F>(lps, codes, scales, x, residual, out, ni, ki, stream);
+  return launch_rows<4, F>(lps, codes, scales, x, residual, out, ni, ki, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_swiglu(const uint8_t* gate, const uint8_t* up, const float* x,
+                              float* out, int64_t n, int64_t k, hipStream_t stream) {
+  return launch_swiglu_fmt<Fmt::kTq2>(gate, up, x, out, n, k, stream);
+}
+
+hipError_t launch_gemv_swiglu_q1(const uint8_t* gate, const uint8_t* up, const float* x,
+                                 float* out, int64_t n, int64_t k, hipStream_t stream) {
+  return launch_swiglu_fmt<Fmt::kQ1>(gate, up, x, out, n, k, stream);
 }
 
 hipError_t launch_gemv_batched(const GemvProblem* probs, int count, int64_t k,
@@ -441,17 +501,12 @@ hipError_t launch_gemv_batched(const GemvProblem* probs, int count, int64_t k,
 
 hipError_t launch_gemv(const uint8_t* soa, const float* x, const float* residual, float* out,
                        int64_t n, int64_t k, hipStream_t stream) {
-  const uint32_t* codes = reinterpret_cast<const uint32_t*>(soa);
-  const uint16_t* scales = reinterpret_cast<const uint16_t*>(soa + scales_offset(n, k));
-  const int lps = lanes_per_slot(k);
-  // Rows per thread: 8 when that still gives >= 2 blocks per CU, else fewer.
-  const int slots = kThreads / lps;
-  int rows = 8;
-  while (rows > 4 && (n + int64_t(slots) * rows - 1) / (int64_t(slots) * rows) < 512) rows >>= 1;
-  if (rows > lps) rows = lps;
-  const int ni = int(n), ki = int(k);
-  if (rows == 8) return launch_rows<8>(lps, codes, scales, x, residual, out, ni, ki, stream);
-  return launch_rows<4>(lps, codes, scales, x, residual, out, ni, ki, stream);
+  return launch_gemv_fmt<Fmt::kTq2>(soa, x, residual, out, n, k, stream);
+}
+
+hipError_t launch_gemv_q1(const uint8_t* soa, const float* x, const float* residual, float* out,
+                          int64_t n, int64_t k, hipStream_t stream) {
+  return launch_gemv_fmt<Fmt::kQ1>(soa, x, residual, out, n, k, stream);
 }
 
 }  // namespace tq2

@@ -41,6 +41,12 @@ EXPORTED_SYMBOLS = (
     "tq2_gemm",
     "tq2_gemm_precise",
     "tq2_gate_up_swiglu",
+    "tq2_q1_aos_bytes",
+    "tq2_q1_soa_bytes",
+    "tq2_q1_reformat_aos_to_soa",
+    "tq2_q1_gemv",
+    "tq2_q1_gemm",
+    "tq2_q1_gate_up_swiglu",
     "tq2_gemm_path",
     "tq2_status_string",
 )
@@ -98,6 +104,18 @@ def _load():
     lib.tq2_gemm_precise.restype = c_int
     lib.tq2_gate_up_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.tq2_gate_up_swiglu.restype = c_int
+    lib.tq2_q1_aos_bytes.argtypes = [i64, i64]
+    lib.tq2_q1_aos_bytes.restype = sz
+    lib.tq2_q1_soa_bytes.argtypes = [i64, i64]
+    lib.tq2_q1_soa_bytes.restype = sz
+    lib.tq2_q1_reformat_aos_to_soa.argtypes = [vp, vp, i64, i64, vp]
+    lib.tq2_q1_reformat_aos_to_soa.restype = c_int
+    lib.tq2_q1_gemv.argtypes = [vp, vp, vp, vp, i64, i64, vp]
+    lib.tq2_q1_gemv.restype = c_int
+    lib.tq2_q1_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.tq2_q1_gemm.restype = c_int
+    lib.tq2_q1_gate_up_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.tq2_q1_gate_up_swiglu.restype = c_int
     lib.tq2_gemm_path.argtypes = [i64, i64, i64]
     lib.tq2_gemm_path.restype = c_int
     lib.tq2_status_string.argtypes = [c_int]
@@ -129,6 +147,23 @@ def aos_bytes(n: int, k: int) -> int:
 
 def soa_bytes(n: int, k: int) -> int:
     return int(lib.tq2_soa_bytes(n, k))
+
+
+def q1_aos_bytes(n: int, k: int) -> int:
+    return int(lib.tq2_q1_aos_bytes(n, k))
+
+
+def q1_soa_bytes(n: int, k: int) -> int:
+    return int(lib.tq2_q1_soa_bytes(n, k))
+
+
+def _sizes(fmt: str):
+    """(aos_bytes, soa_bytes) functions of a weight format ("tq2" or "q1")."""
+    if fmt == "tq2":
+        return aos_bytes, soa_bytes
+    if fmt == "q1":
+        return q1_aos_bytes, q1_soa_bytes
+    raise ValueError("unknown weight format %r" % (fmt,))
 
 
 def soa_layout_version() -> int:
@@ -176,6 +211,29 @@ def gemm_precise_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, 
                                     stream or None))
 
 
+def q1_reformat_aos_to_soa_ptr(aos_ptr: int, soa_ptr: int, n: int, k: int,
+                               stream: int = 0) -> int:
+    return int(lib.tq2_q1_reformat_aos_to_soa(aos_ptr, soa_ptr, n, k, stream or None))
+
+
+def q1_gemv_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, n: int, k: int,
+                stream: int = 0) -> int:
+    return int(lib.tq2_q1_gemv(soa_ptr, x_ptr, residual_ptr or None, out_ptr, n, k,
+                               stream or None))
+
+
+def q1_gemm_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, n: int,
+                k: int, stream: int = 0) -> int:
+    return int(lib.tq2_q1_gemm(soa_ptr, x_ptr, residual_ptr or None, out_ptr, m, n, k,
+                               stream or None))
+
+
+def q1_gate_up_swiglu_ptr(gate_ptr: int, up_ptr: int, x_ptr: int, out_ptr: int, m: int, n: int,
+                          k: int, stream: int = 0) -> int:
+    return int(lib.tq2_q1_gate_up_swiglu(gate_ptr or None, up_ptr or None, x_ptr or None,
+                                         out_ptr or None, m, n, k, stream or None))
+
+
 def gate_up_swiglu_ptr(gate_ptr: int, up_ptr: int, x_ptr: int, out_ptr: int, m: int, n: int,
                        k: int, stream: int = 0) -> int:
     return int(lib.tq2_gate_up_swiglu(gate_ptr or None, up_ptr or None, x_ptr or None,
@@ -210,52 +268,59 @@ def _require(t, dtype, numel: int, what: str):
         raise ValueError("%s must have %d elements, got %d" % (what, numel, t.numel()))
 
 
-def reformat_aos_to_soa(aos, n: int, k: int, out=None):
-    """AoS block bytes (uint8 device tensor) -> resident SoA weight (uint8)."""
+def reformat_aos_to_soa(aos, n: int, k: int, out=None, fmt: str = "tq2"):
+    """AoS block bytes (uint8 device tensor) -> resident SoA weight (uint8).
+    fmt: "tq2" (34-byte TQ2_0_g128 blocks) or "q1" (18-byte Q1_g128 blocks)."""
     torch = _torch()
-    nbytes = aos_bytes(n, k)
+    aos_b, soa_b = _sizes(fmt)
+    nbytes = aos_b(n, k)
     if nbytes == 0 and n != 0:
         _check(TQ2_ERR_SHAPE if k > 0 else TQ2_ERR_INVALID, "reformat_aos_to_soa")
     _require(aos, torch.uint8, nbytes, "aos")
     if out is None:
-        out = torch.empty(soa_bytes(n, k), dtype=torch.uint8, device=aos.device)
-    _require(out, torch.uint8, soa_bytes(n, k), "soa")
-    _check(reformat_aos_to_soa_ptr(aos.data_ptr(), out.data_ptr(), n, k,
-                                   _stream_handle(aos.device)), "reformat_aos_to_soa")
+        out = torch.empty(soa_b(n, k), dtype=torch.uint8, device=aos.device)
+    _require(out, torch.uint8, soa_b(n, k), "soa")
+    call = q1_reformat_aos_to_soa_ptr if fmt == "q1" else reformat_aos_to_soa_ptr
+    _check(call(aos.data_ptr(), out.data_ptr(), n, k, _stream_handle(aos.device)),
+           "reformat_aos_to_soa")
     return out
 
 
-def gemv(soa, x, n: int, k: int, residual=None, out=None):
+def gemv(soa, x, n: int, k: int, residual=None, out=None, fmt: str = "tq2"):
     """out[n] = residual[n] + sum_k x[k] * w[n, k]; x is f32 [k] (or [1, k])."""
     torch = _torch()
-    _require(soa, torch.uint8, soa_bytes(n, k), "soa")
+    _require(soa, torch.uint8, _sizes(fmt)[1](n, k), "soa")
     _require(x, torch.float32, k, "x")
     if residual is not None:
         _require(residual, torch.float32, n, "residual")
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=x.device)
     _require(out, torch.float32, n, "out")
-    _check(gemv_ptr(soa.data_ptr(), x.data_ptr(),
-                    residual.data_ptr() if residual is not None else 0,
-                    out.data_ptr(), n, k, _stream_handle(x.device)), "gemv")
+    call = q1_gemv_ptr if fmt == "q1" else gemv_ptr
+    _check(call(soa.data_ptr(), x.data_ptr(), residual.data_ptr() if residual is not None else 0,
+                out.data_ptr(), n, k, _stream_handle(x.device)), "gemv")
     return out
 
 
-def gemm(soa, x, n: int, k: int, residual=None, out=None, precise: bool = False):
+def gemm(soa, x, n: int, k: int, residual=None, out=None, precise: bool = False,
+         fmt: str = "tq2"):
     """out[m, n] = residual[m, n] + sum_k x[m, k] * w[n, k]; x is f32 [m, k].
-    precise=True calls tq2_gemm_precise (f32-class accuracy at every M)."""
+    precise=True calls tq2_gemm_precise (f32-class accuracy at every M; TQ2
+    only)."""
     torch = _torch()
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x must be [m, %d]" % k)
+    if precise and fmt != "tq2":
+        raise ValueError("precise=True is a TQ2 entry point")
     m = x.shape[0]
-    _require(soa, torch.uint8, soa_bytes(n, k), "soa")
+    _require(soa, torch.uint8, _sizes(fmt)[1](n, k), "soa")
     _require(x, torch.float32, m * k, "x")
     if residual is not None:
         _require(residual, torch.float32, m * n, "residual")
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _require(out, torch.float32, m * n, "out")
-    call = gemm_precise_ptr if precise else gemm_ptr
+    call = q1_gemm_ptr if fmt == "q1" else (gemm_precise_ptr if precise else gemm_ptr)
     _check(call(soa.data_ptr(), x.data_ptr(), residual.data_ptr() if residual is not None else 0,
                 out.data_ptr(), m, n, k, _stream_handle(x.device)),
            "gemm_precise" if precise else "gemm")
@@ -288,19 +353,20 @@ def gemv_batched(problems):
     return outs
 
 
-def gate_up_swiglu(gate_soa, up_soa, x, n: int, k: int, out=None):
+def gate_up_swiglu(gate_soa, up_soa, x, n: int, k: int, out=None, fmt: str = "tq2"):
     """out[m, n] = silu(x W_gate^T)[m, n] * (x W_up^T)[m, n]; x is f32 [m, k]."""
     torch = _torch()
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x must be [m, %d]" % k)
     m = x.shape[0]
-    _require(gate_soa, torch.uint8, soa_bytes(n, k), "gate_soa")
-    _require(up_soa, torch.uint8, soa_bytes(n, k), "up_soa")
+    sb = _sizes(fmt)[1](n, k)
+    _require(gate_soa, torch.uint8, sb, "gate_soa")
+    _require(up_soa, torch.uint8, sb, "up_soa")
     _require(x, torch.float32, m * k, "x")
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _require(out, torch.float32, m * n, "out")
-    _check(gate_up_swiglu_ptr(gate_soa.data_ptr(), up_soa.data_ptr(), x.data_ptr(),
-                              out.data_ptr(), m, n, k, _stream_handle(x.device)),
-           "gate_up_swiglu")
+    call = q1_gate_up_swiglu_ptr if fmt == "q1" else gate_up_swiglu_ptr
+    _check(call(gate_soa.data_ptr(), up_soa.data_ptr(), x.data_ptr(), out.data_ptr(), m, n, k,
+                _stream_handle(x.device)), "gate_up_swiglu")
     return out

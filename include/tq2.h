@@ -170,6 +170,44 @@ int tq2_gemm_precise(const void* soa, const float* x, const float* residual, flo
 int tq2_gate_up_swiglu(const void* gate_soa, const void* up_soa, const float* x, float* out,
                        int64_t m, int64_t n, int64_t k, void* stream);
 
+/* ---- Q1_g128: the 1-bit sibling format --------------------------------------
+ * The pages' decode and prefill kernels for 1-bit weights (oxibonsai-kernels
+ * 0.1.5, pipelines.rs, `MetalPipelines` fields `gemv_q1_g128_v7`,
+ * `gemv_q1_g128_v7_residual`, `gemm_q1_g128_v7`, `gemm_q1_g128_v7_residual`,
+ * `fused_gate_up_swiglu_q1`, `fused_gate_up_swiglu_gemm_q1`) run on a format
+ * the pages name but do not lay out.  Recorded reading, mirroring the TQ2
+ * block: 128 weights per block in 18 bytes, `qs[16]` then a little-endian
+ * binary16 `d`; weight j has bit (qs[j / 8] >> (j % 8)) & 1, and a set bit is
+ * +d, a clear bit -d.  The operations, arguments, path choice (tq2_gemm_path),
+ * tolerances, aliasing rules and errors are those of the TQ2 entry points
+ * above; only the weight buffers differ (sizes from tq2_q1_aos_bytes /
+ * tq2_q1_soa_bytes, a private SoA layout of the same version number). */
+
+/* Bytes of an [n, k] Q1_g128 weight in AoS blocks: n * (k/128) * 18, or 0 for
+ * invalid n, k. */
+size_t tq2_q1_aos_bytes(int64_t n, int64_t k);
+
+/* Bytes of the library's resident Q1 SoA copy (a multiple of 256), or 0. */
+size_t tq2_q1_soa_bytes(int64_t n, int64_t k);
+
+/* Q1 AoS -> SoA, as tq2_reformat_aos_to_soa. */
+int tq2_q1_reformat_aos_to_soa(const void* aos, void* soa, int64_t n, int64_t k, void* stream);
+
+/* Q1 decode GEMV (M = 1) with optional residual, as tq2_gemv (the pages'
+ * `gemv_q1_g128_v7` / `gemv_q1_g128_v7_residual`). */
+int tq2_q1_gemv(const void* soa, const float* x, const float* residual, float* out,
+                int64_t n, int64_t k, void* stream);
+
+/* Q1 matmul for any M >= 1 with optional residual, as tq2_gemm (the pages'
+ * `gemm_q1_g128_v7` / `gemm_q1_g128_v7_residual`, with no cap on M). */
+int tq2_q1_gemm(const void* soa, const float* x, const float* residual, float* out,
+                int64_t m, int64_t n, int64_t k, void* stream);
+
+/* Q1 fused gate/up projections + SwiGLU, as tq2_gate_up_swiglu (the pages'
+ * `fused_gate_up_swiglu_q1` / `fused_gate_up_swiglu_gemm_q1`). */
+int tq2_q1_gate_up_swiglu(const void* gate_soa, const void* up_soa, const float* x, float* out,
+                          int64_t m, int64_t n, int64_t k, void* stream);
+
 /* The kernel tq2_gemm uses for this shape (0, 1 or 2 as listed above), or
  * TQ2_ERR_INVALID / TQ2_ERR_SHAPE for an invalid shape.  Pure host function. */
 int tq2_gemm_path(int64_t m, int64_t n, int64_t k);

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 17
     assert sorted(tq2.EXPORTED_SYMBOLS) == names
     lib = ctypes.CDLL(tq2.LIB_PATH)
     for name in names:
@@ -147,6 +147,33 @@ def test_swiglu_checks_before_any_device_work():
     assert sw(0, 0, 0, 0, 4, 0, 128) == tq2.TQ2_OK
 
 
+def test_q1_sizes_and_checks():
+    assert tq2.q1_aos_bytes(1, 128) == 18
+    assert tq2.q1_aos_bytes(4096, 4096) == 2359296
+    for bad in [(1, 100), (1, 0), (-1, 128)]:
+        assert tq2.q1_aos_bytes(*bad) == 0 and tq2.q1_soa_bytes(*bad) == 0
+    for n, k in [(1, 128), (3, 384), (4096, 4096), (77, 12288)]:
+        s = tq2.q1_soa_bytes(n, k)
+        assert s % 256 == 0
+        assert n * k // 8 + n * (k // 128) * 2 <= s < n * k // 8 + n * (k // 128) * 2 + 512
+    r, v, g = tq2.q1_reformat_aos_to_soa_ptr, tq2.q1_gemv_ptr, tq2.q1_gemm_ptr
+    X, O = A + 0x100000, A + 0x200000
+    assert r(A + 1, X, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert r(A + 0x1C0, A + 0x200, 8, 128) == tq2.TQ2_ERR_ALIAS     # 144 B of AoS over soa
+    assert r(A, A + 160, 8, 128) == tq2.TQ2_ERR_ALIGN
+    assert r(0, 0, 0, 128) == tq2.TQ2_OK
+    assert v(A, X, 0, O, 8, 200) == tq2.TQ2_ERR_SHAPE
+    assert v(A, X, 0, X, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert g(A + 64, X, 0, O, 4, 8, 128) == tq2.TQ2_ERR_ALIGN
+    # the Q1 weight (8 rows x 16 B of bits + scales, 512 B) vs out
+    assert g(A, X, 0, A + 256, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+    assert g(A, X, 0, A + 512, 4, 8, 128) != tq2.TQ2_ERR_ALIAS
+    assert g(0, 0, 0, 0, 0, 8, 128) == tq2.TQ2_OK
+    sw = tq2.q1_gate_up_swiglu_ptr
+    assert sw(A, A + 0x40000, X, O, 4, 8, 100) == tq2.TQ2_ERR_SHAPE
+    assert sw(A, A + 0x40000, X, A + 0x40000, 4, 8, 128) == tq2.TQ2_ERR_ALIAS
+
+
 def test_device_check_without_gpu():
     """Valid arguments but no gfx950 device: the call must return
     TQ2_ERR_DEVICE (never crash).  Only meaningful where no GPU is visible."""
@@ -155,6 +182,8 @@ def test_device_check_without_gpu():
         pytest.skip("a GPU is visible; this check is for GPU-less hosts")
     st = tq2.gemm_ptr(A, A + 0x100000, 0, A + 0x200000, 4, 8, 128)
     assert st == tq2.TQ2_ERR_DEVICE
+    assert tq2.q1_gemm_ptr(A, A + 0x100000, 0, A + 0x200000, 4, 8, 128) == tq2.TQ2_ERR_DEVICE
+    assert tq2.q1_reformat_aos_to_soa_ptr(A, A + 0x100000, 8, 128) == tq2.TQ2_ERR_DEVICE
     # gate and up may be the same buffer
     assert tq2.gate_up_swiglu_ptr(A, A, A + 0x100000, A + 0x200000, 1, 8, 128) == \
         tq2.TQ2_ERR_DEVICE
