@@ -25,10 +25,11 @@
 // added in LDS and with cross-lane shuffles, and the residual is added last.
 //
 // Q1_g128 weights (the pages' `gemv_q1_g128_v7` / `_residual` decode kernels,
-// same table) run the same kernels with F = Fmt::kQ1: a lane's word holds 32
-// weights, each pair's two bits are shifted onto the binary16 sign positions
-// and OR-ed with 1.0, giving the exact pair ((-1)^b, (-1)^b'), and the 32-term
-// sum is scaled by -d.
+// same table) run the same kernels with F = Fmt::kQ1.  A lane still owns 16
+// consecutive weights: half of a 32-bit word (two lanes read the same word;
+// the odd one shifts it right by 8).  Each pair's two bits are shifted onto
+// the binary16 sign positions and OR-ed with 1.0, giving the exact pair
+// ((-1)^b, (-1)^b'), and the 16-term sum is scaled by -d.
 #include "tq2_internal.h"
 
 namespace tq2 {
@@ -63,9 +64,17 @@ __device__ __forceinline__ void decode_word(uint32_t w, uint32_t magic, half2_t 
   }
 }
 
-// Weights per 32-bit code word of the SoA codes plane.
+// Code words per weight row, and the code word of lane unit u (16 weights):
+// TQ2 word u; Q1 half (u & 1) of word u >> 1, moved to the low byte of each
+// half-word so that pair r of the unit sits at bits r and r + 16.
 template <Fmt F>
-constexpr int kWpw = F == Fmt::kQ1 ? 32 : 16;
+__device__ __forceinline__ int words_per_row(int k) { return F == Fmt::kQ1 ? k >> 5 : k >> 4; }
+
+template <Fmt F>
+__device__ __forceinline__ uint32_t unit_word(const uint32_t* crow, unsigned u) {
+  if constexpr (F == Fmt::kQ1) return crow[u >> 1] >> (8 * (u & 1));
+  return crow[u];
+}
 
 __device__ __forceinline__ float dot16(const half2_t (&v)[8], const float (&xv)[16]) {
   float s0 = 0.f, s1 = 0.f;
@@ -77,13 +86,13 @@ __device__ __forceinline__ float dot16(const half2_t (&v)[8], const float (&xv)[
   return s0 + s1;
 }
 
-// Sum of x[t] * (2 b_t - 1) over the 32 weights of one Q1 word (exact +-1
+// Sum of x[t] * (2 b_t - 1) over the 16 weights of one Q1 unit (exact +-1
 // pairs, f32 products and sums).
-__device__ __forceinline__ float dot32_q1(uint32_t w, const float (&xv)[32]) {
+__device__ __forceinline__ float dot16_q1(uint32_t w, const float (&xv)[16]) {
   const uint32_t one = 0x3C003C00u;             // binary16 pair (1, 1)
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
+  for (int p = 0; p < 8; ++p) {
     const half2_t v = __builtin_bit_cast(half2_t, and_or(w << (15 - p), 0x80008000u, one));
     s0 = __builtin_fmaf(xv[2 * p], float(v[0]), s0);
     s1 = __builtin_fmaf(xv[2 * p + 1], float(v[1]), s1);
@@ -91,25 +100,27 @@ __device__ __forceinline__ float dot32_q1(uint32_t w, const float (&xv)[32]) {
   return -(s0 + s1);                            // (-1)^b = -(2b - 1)
 }
 
-// Load ROWS code words and scales of word wc, and the kWpw x values of it.
+// Load ROWS code words and scales of lane unit wc (16 weights), and the 16 x
+// values of it.
 template <int ROWS, Fmt F>
 __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
                                              const uint16_t* __restrict__ scales,
                                              const float* __restrict__ x, int row0, int n_rows,
-                                             int wpr, int kb_count, int wc, uint32_t (&cw)[ROWS],
-                                             uint32_t (&db)[ROWS], float (&xv)[kWpw<F>]) {
+                                             int k, int kb_count, int wc, uint32_t (&cw)[ROWS],
+                                             uint32_t (&db)[ROWS], float (&xv)[16]) {
   const unsigned uwc = unsigned(wc);            // lane offset: 32-bit, base pointer uniform
+  const int wrow = words_per_row<F>(k);
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const int row = min(row0 + r, n_rows - 1);
-    const uint32_t* crow = codes + size_t(row) * wpr;
+    const uint32_t* crow = codes + size_t(row) * wrow;
     const uint16_t* srow = scales + size_t(row) * kb_count;
-    cw[r] = crow[uwc];
-    db[r] = srow[uwc / (kBlockWeights / kWpw<F>)];
+    cw[r] = unit_word<F>(crow, uwc);
+    db[r] = srow[uwc >> 3];
   }
-  const float4* xp = reinterpret_cast<const float4*>(x + kWpw<F> * wc);
+  const float4* xp = reinterpret_cast<const float4*>(x + 16 * wc);
 #pragma unroll
-  for (int i = 0; i < kWpw<F> / 4; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const float4 q = xp[i];
     xv[4 * i] = q.x;
     xv[4 * i + 1] = q.y;
@@ -121,7 +132,7 @@ __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
 template <int ROWS, Fmt F>
 __device__ __forceinline__ void accumulate_segment(const uint32_t (&cw)[ROWS],
                                                    const uint32_t (&db)[ROWS],
-                                                   const float (&xv)[kWpw<F>], bool live,
+                                                   const float (&xv)[16], bool live,
                                                    float (&part)[ROWS]) {
   const uint32_t magic = kMagic;
 #pragma unroll
@@ -129,7 +140,7 @@ __device__ __forceinline__ void accumulate_segment(const uint32_t (&cw)[ROWS],
     const float d = float(__builtin_bit_cast(_Float16, uint16_t(db[r])));
     float s;
     if constexpr (F == Fmt::kQ1) {
-      s = dot32_q1(cw[r], xv) * d;
+      s = dot16_q1(cw[r], xv) * d;
     } else {
       half2_t v[8];
       decode_word(cw[r], magic, v);
@@ -156,7 +167,7 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
   // With one slot per block the row indices are block-uniform (scalar).
   const int slot = SLOTS == 1 ? 0 : t / LPS;
   const int lw = SLOTS == 1 ? t : t % LPS;      // word index inside a K segment
-  const int wpr = k / kWpw<F>;                  // code words per row
+  const int wpr = k >> 4;                       // lane units (16 weights) per row
   const int kb_count = k >> 7;
   const int row0 = blk * OUTS + slot * ROWS;
 
@@ -166,14 +177,14 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
 
   uint32_t cw[ROWS];
   uint32_t db[ROWS];
-  float xv[kWpw<F>];
+  float xv[16];
   if constexpr (ONE_SEG) {
-    if (wpr == LPS) {                           // every lane has a word: no masking
-      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, wpr, kb_count, lw, cw, db, xv);
+    if (wpr == LPS) {                           // every lane has a unit: no masking
+      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, k, kb_count, lw, cw, db, xv);
       accumulate_segment<ROWS, F>(cw, db, xv, true, part);
     } else {
       const bool live = lw < wpr;
-      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, wpr, kb_count, live ? lw : wpr - 1,
+      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, k, kb_count, live ? lw : wpr - 1,
                             cw, db, xv);
       accumulate_segment<ROWS, F>(cw, db, xv, live, part);
     }
@@ -181,7 +192,7 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
     for (int seg = 0; seg < wpr; seg += LPS) {
       const int w = seg + lw;
       const bool live = w < wpr;
-      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, wpr, kb_count, live ? w : wpr - 1,
+      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, k, kb_count, live ? w : wpr - 1,
                             cw, db, xv);
       accumulate_segment<ROWS, F>(cw, db, xv, live, part);
     }
@@ -267,7 +278,8 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   const int t = threadIdx.x;
   const int slot = SLOTS == 1 ? 0 : t / LPS;
   const int lw = SLOTS == 1 ? t : t % LPS;
-  const int wpr = k / kWpw<F>;
+  const int wpr = k >> 4;                       // lane units (16 weights) per row
+  const int wrow = words_per_row<F>(k);
   const int kb_count = k >> 7;
   const int out0 = blockIdx.x * OUTS + slot * HALF;
 
@@ -276,21 +288,21 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   for (int r = 0; r < ROWS; ++r) part[r] = 0.f;
   uint32_t cw[ROWS];
   uint32_t db[ROWS];
-  float xv[kWpw<F>];
+  float xv[16];
   // Rows 0..HALF-1 from the gate weight, HALF..ROWS-1 from the up weight.
   auto load = [&](int wc) {
     const unsigned uwc = unsigned(wc);
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const int row = min(out0 + (r % HALF), n_rows - 1);
-      const uint32_t* crow = (r < HALF ? gcodes : ucodes) + size_t(row) * wpr;
+      const uint32_t* crow = (r < HALF ? gcodes : ucodes) + size_t(row) * wrow;
       const uint16_t* srow = (r < HALF ? gscales : uscales) + size_t(row) * kb_count;
-      cw[r] = crow[uwc];
-      db[r] = srow[uwc / (kBlockWeights / kWpw<F>)];
+      cw[r] = unit_word<F>(crow, uwc);
+      db[r] = srow[uwc >> 3];
     }
-    const float4* xp = reinterpret_cast<const float4*>(x + kWpw<F> * wc);
+    const float4* xp = reinterpret_cast<const float4*>(x + 16 * wc);
 #pragma unroll
-    for (int i = 0; i < kWpw<F> / 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const float4 q = xp[i];
       xv[4 * i] = q.x;
       xv[4 * i + 1] = q.y;
@@ -352,7 +364,7 @@ hipError_t launch_rows(int lps, const uint32_t* codes, const uint16_t* scales, c
     TQ2_GEMV_CASE(64)
     TQ2_GEMV_CASE(128)
     default:
-      if (k / kWpw<F> <= 256)
+      if (k / 16 <= 256)
         hipLaunchKernelGGL((gemv_kernel<ROWS, 256, true, F>), grid, dim3(kThreads), 0, stream,
                            codes, scales, x, residual, out, n, k);
       else
@@ -392,9 +404,9 @@ hipError_t launch_batched_rows(int lps, const GemvBatchArgs& args, int blocks, i
   return hipGetLastError();
 }
 
-// Lanes per row slot for a given k: a power of two >= k/kWpw, at most 256.
-int lanes_per_slot(int64_t k, Fmt f = Fmt::kTq2) {
-  const int64_t wpr = k / (f == Fmt::kQ1 ? 32 : 16);
+// Lanes per row slot for a given k: a power of two >= k/16, at most 256.
+int lanes_per_slot(int64_t k) {
+  const int64_t wpr = k / 16;
   int lps = 8;
   while (lps < wpr && lps < kThreads) lps <<= 1;
   return lps;
@@ -411,7 +423,7 @@ hipError_t launch_swiglu_fmt(const uint8_t* gate, const uint8_t* up, const float
   const uint16_t* gs = reinterpret_cast<const uint16_t*>(gate + scales_offset(F, n, k));
   const uint32_t* uc = reinterpret_cast<const uint32_t*>(up);
   const uint16_t* us = reinterpret_cast<const uint16_t*>(up + scales_offset(F, n, k));
-  const int lps = lanes_per_slot(k, F);
+  const int lps = lanes_per_slot(k);
   const int outs = (kThreads / lps) * 4;
   const int64_t blocks = (n + outs - 1) / outs;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -429,7 +441,7 @@ hipError_t launch_swiglu_fmt(const uint8_t* gate, const uint8_t* up, const float
     TQ2_SWIGLU_CASE(64)
     TQ2_SWIGLU_CASE(128)
     default:
-      if (k / kWpw<F> <= 256)
+      if (k / 16 <= 256)
         hipLaunchKernelGGL((gemv_swiglu_kernel<256, true, F>), grid, dim3(kThreads), 0, stream,
                            gc, gs, uc, us, x, out, ni, ki);
       else
@@ -446,7 +458,7 @@ hipError_t launch_gemv_fmt(const uint8_t* soa, const float* x, const float* resi
                            int64_t n, int64_t k, hipStream_t stream) {
   const uint32_t* codes = reinterpret_cast<const uint32_t*>(soa);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(soa + scales_offset(F, n, k));
-  const int lps = lanes_per_slot(k, F);
+  const int lps = lanes_per_slot(k);
   // Rows per thread: 8 when that still gives >= 2 blocks per CU, else fewer.
   const int slots = kThreads / lps;
   int rows = 8;
