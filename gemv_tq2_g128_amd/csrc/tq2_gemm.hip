@@ -124,6 +124,49 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Store an MT x NO f32 result tile, staged row-major in LDS with row pitch
+// NO + 4, to out[m0 + r][n0 + c] (plus the residual): THREADS threads walk
+// the tile in whole rows, 16 bytes per lane, so each store instruction
+// writes contiguous row segments.  The output is written once and not read
+// again here, so the full-vector stores are non-temporal.
+template <int MT, int NO, int THREADS>
+__device__ __forceinline__ void store_tile(const float* tile, int tid, int m0, int n0, int M,
+                                           int N, const float* __restrict__ residual,
+                                           float* __restrict__ out) {
+  constexpr int TP = NO + 4;
+  constexpr int C4 = NO / 4;             // float4 per tile row
+  const bool vec = (N & 3) == 0;
+#pragma unroll
+  for (int it = 0; it < (MT * C4 + THREADS - 1) / THREADS; ++it) {
+    const int idx = tid + THREADS * it;
+    if ((MT * C4) % THREADS != 0 && idx >= MT * C4) break;
+    const int r = idx / C4;
+    const int c4 = idx - r * C4;
+    const int m = m0 + r, n = n0 + 4 * c4;
+    if (m >= M || n >= N) continue;
+    const float4 t4 = *reinterpret_cast<const float4*>(&tile[r * TP + 4 * c4]);
+    const size_t o = size_t(m) * N + n;
+    if (vec && n + 3 < N) {
+      floatx4_t v = {t4.x, t4.y, t4.z, t4.w};
+      if (residual) {
+        const float4 rr = *reinterpret_cast<const float4*>(residual + o);
+        v = floatx4_t{rr.x + v[0], rr.y + v[1], rr.z + v[2], rr.w + v[3]};
+      }
+      __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t*>(out + o));
+    } else {
+      const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e < N) {
+          float v = tv[e];
+          if (residual) v = residual[o + e] + v;
+          out[o + e] = v;
+        }
+      }
+    }
+  }
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -386,9 +429,9 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
   }
 
   // ---- K-split reduction: the wk = 1 waves hand their sums to wk = 0 -----
+  float* red = reinterpret_cast<float*>(&As[0][0][0][0]);
+  static_assert(WN * RT * CG * 4 * 64 * 4 <= sizeof(As), "reduction buffer");
   if constexpr (WK == 2) {
-    float* red = reinterpret_cast<float*>(&As[0][0][0][0]);
-    static_assert(WN * RT * CG * 4 * 64 * 4 <= sizeof(As), "reduction buffer");
     if (wk == 1) {
 #pragma unroll
       for (int i = 0; i < RT; ++i)
@@ -399,9 +442,6 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
             red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
     }
     __syncthreads();
-    if constexpr (!SWIGLU) {
-      if (wk == 1) return;
-    }
     if (wk == 0) {
 #pragma unroll
       for (int i = 0; i < RT; ++i)
@@ -415,8 +455,6 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
 
   // ---- SwiGLU: each up wave hands its sums to the gate wave of its columns -
   if constexpr (SWIGLU) {
-    float* red = reinterpret_cast<float*>(&As[0][0][0][0]);
-    static_assert(WN * RT * CG * 4 * 64 * 4 <= sizeof(As), "exchange buffer");
     // An up wave overwrites only the slots its own lanes have just read.
     if (wk == 0 && upw) {
 #pragma unroll
@@ -428,50 +466,38 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
             red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
     }
     __syncthreads();
-    if (wk != 0 || upw) return;
-    const int wu = wn + WN / 2;
+    if (wk == 0 && !upw) {
+      const int wu = wn + WN / 2;
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
+      for (int i = 0; i < RT; ++i)
 #pragma unroll
-      for (int j = 0; j < CG; ++j)
+        for (int j = 0; j < CG; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[i][j][e] = silu(acc[i][j][e]) * red[(((wu * RT + i) * CG + j) * 4 + e) * 64 + lane];
+          for (int e = 0; e < 4; ++e)
+            acc[i][j][e] =
+                silu(acc[i][j][e]) * red[(((wu * RT + i) * CG + j) * 4 + e) * 64 + lane];
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------
   // The weight operand is the MFMA's first (row) operand, so each 16x16
-  // result holds D[n = 4g + e][m = col]: a lane owns four consecutive output
-  // columns of one row and writes them (and reads the residual) as one
-  // 16-byte access when the row pitch allows it.
-  const bool vec = (N & 3) == 0;
+  // result holds D[n = 4g + e][m = col]: the waves holding finished sums lay
+  // them out row-major in LDS (tile row i * 16 + col, columns
+  // wc * NW + j * 16 + 4g .. + 3), and every thread then stores whole rows.
+  constexpr int TP = NT + 4;
+  static_assert(MT * TP * 4 <= sizeof(As), "output tile");
+  float* tile = red;
+  __syncthreads();                       // every read of the reduction slots is done
+  if (wk == 0 && !upw) {
 #pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    const int m = m0 + i * 16 + col;
-    if (m >= M) continue;
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < CG; ++j) {
-      const int n = n0 + wc * NW + j * 16 + 4 * g;
-      const size_t o = size_t(m) * N + n;
-      if (vec && n + 3 < N) {
-        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (residual) {
-          const float4 r = *reinterpret_cast<const float4*>(residual + o);
-          v = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
-        }
-        *reinterpret_cast<float4*>(out + o) = v;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (n + e < N) {
-            float v = acc[i][j][e];
-            if (residual) v = residual[o + e] + v;
-            out[o + e] = v;
-          }
-        }
-      }
-    }
+      for (int j = 0; j < CG; ++j)
+        *reinterpret_cast<float4*>(&tile[(i * 16 + col) * TP + wc * NW + j * 16 + 4 * g]) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
   }
+  __syncthreads();
+  store_tile<MT, NT, THREADS>(tile, tid, m0, n0, M, N, residual, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,7 +796,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     }
   }
 
-  // ---- group 1 hands its partial sums to group 0 --------------------------
+  // ---- epilogue ----------------------------------------------------------------
+  // Group 1 hands its partial sums to group 0 through LDS (and, for SwiGLU,
+  // group 0's up waves hand theirs to the gate waves).  The finished MT x NO
+  // tile is then laid out row-major in LDS, and all 512 threads store it in
+  // whole rows, 16 bytes per lane, reading the residual the same way.
   float* red = reinterpret_cast<float*>(&As[0][0][0]);
   static_assert(4 * RT * CG * 4 * 64 * 4 <= sizeof(As), "reduction buffer");
   if (grp == 1) {
@@ -783,9 +813,6 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
           red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
   }
   __syncthreads();
-  if constexpr (!SWIGLU) {
-    if (grp == 1) return;
-  }
   if (grp == 0) {
 #pragma unroll
     for (int i = 0; i < RT; ++i)
@@ -796,8 +823,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
           acc[i][j][e] += red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane];
   }
   if constexpr (SWIGLU) {
-    // Group 0's up waves hand their sums to the gate waves of their columns
-    // (each overwrites only the slots its own lanes have just read).
+    // Each up wave overwrites only the slots its own lanes have just read.
     if (grp == 0 && upw) {
 #pragma unroll
       for (int i = 0; i < RT; ++i)
@@ -808,45 +834,34 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
             red[(((wn * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
     }
     __syncthreads();
-    if (grp == 1 || upw) return;
+    if (grp == 0 && !upw) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j][e] =
+                silu(acc[i][j][e]) * red[((((wn + 2) * RT + i) * CG + j) * 4 + e) * 64 + lane];
+    }
+  }
+
+  // Row-major staging: D[n = 4g + e][m = col] of each 16 x 16 result goes to
+  // tile row i * 16 + col, columns wc * NW + j * 16 + 4g .. + 3.
+  constexpr int TP = NO + 4;             // tile row pitch in floats
+  static_assert(MT * TP * 4 <= sizeof(As), "output tile");
+  float* tile = red;
+  __syncthreads();                       // every read of the reduction slots is done
+  if (grp == 0 && !upw) {
 #pragma unroll
     for (int i = 0; i < RT; ++i)
 #pragma unroll
       for (int j = 0; j < CG; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[i][j][e] =
-              silu(acc[i][j][e]) * red[((((wn + 2) * RT + i) * CG + j) * 4 + e) * 64 + lane];
+        *reinterpret_cast<float4*>(&tile[(i * 16 + col) * TP + wc * NW + j * 16 + 4 * g]) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
   }
-
-  const bool vec = (N & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < RT; ++i) {
-    const int m = m0 + i * 16 + col;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < CG; ++j) {
-      const int n = n0 + wc * NW + j * 16 + 4 * g;
-      const size_t o = size_t(m) * N + n;
-      if (vec && n + 3 < N) {
-        float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        if (residual) {
-          const float4 r = *reinterpret_cast<const float4*>(residual + o);
-          v = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
-        }
-        *reinterpret_cast<float4*>(out + o) = v;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (n + e < N) {
-            float v = acc[i][j][e];
-            if (residual) v = residual[o + e] + v;
-            out[o + e] = v;
-          }
-        }
-      }
-    }
-  }
+  __syncthreads();
+  store_tile<MT, NO, 512>(tile, tid, m0, n0, M, N, residual, out);
 }
 
 // `up` is null for the plain matmul; with SWIGLU, `soa` is the gate weight.
