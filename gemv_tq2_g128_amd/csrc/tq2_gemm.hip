@@ -594,20 +594,47 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     }
   };
 
-  // Weights: lane's column, its k-group g, this group's half of the steps.
+  // Weights: lane's column and k-group g.  Group 0 loads the code words of
+  // both groups' halves of the steps (one 2*QW-dword load per column group,
+  // twice the bytes per instruction of a per-group load) and hands group 1's
+  // half over through LDS one phase later; group 1 issues no weight loads.
+  // cw[j][0 .. QW) is the calling group's half.
   const uint32_t nl = uint32_t(n0 + wc * NW + col);
-  const uint32_t code_voff = nl * row_bytes + 8u * BITS * uint32_t(g) + 4u * QW * uint32_t(grp);
-  uint32_t cw[CG][QW];
-  auto load_w = [&](int c) {
+  const uint32_t code_voff = nl * row_bytes + 8u * BITS * uint32_t(g);
+  uint32_t cw[CG][2 * QW];
+  __shared__ uint32_t Hw[4 * CG * 64 * QW];    // hand-over: [wn][j][lane][QW]
+  auto load_w = [&](int c) {                   // group 0
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
       const uint32_t off = code_voff + uint32_t(j * 16) * row_bytes + uint32_t(c * 32 * BITS);
       if constexpr (QW == 2) {
-        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
-        cw[j][0] = v[0];
-        cw[j][1] = v[1];
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+        cw[j][0] = v[0]; cw[j][1] = v[1]; cw[j][2] = v[2]; cw[j][3] = v[3];
       } else {
-        cw[j][0] = __builtin_amdgcn_raw_buffer_load_b32(rc, off, 0, 0);
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
+        cw[j][0] = v[0]; cw[j][1] = v[1];
+      }
+    }
+  };
+  auto hand_over = [&]() {                     // group 0: group 1's half into LDS
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      uint32_t* h = &Hw[((wn * CG + j) * 64 + lane) * QW];
+      if constexpr (QW == 2)
+        *reinterpret_cast<u32x2_t*>(h) = u32x2_t{cw[j][2], cw[j][3]};
+      else
+        *h = cw[j][1];
+    }
+  };
+  auto take_over = [&]() {                     // group 1: its half from LDS
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const uint32_t* h = &Hw[((wn * CG + j) * 64 + lane) * QW];
+      if constexpr (QW == 2) {
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(h);
+        cw[j][0] = v[0]; cw[j][1] = v[1];
+      } else {
+        cw[j][0] = *h;
       }
     }
   };
@@ -727,20 +754,31 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
 #pragma unroll
     for (int j = 0; j < CG; ++j) asm volatile("" ::"v"(wlast[j]), "v"(dlast[j]));
   };
-  // Memory phase: decode chunk cd's weights (registers loaded one chunk ago),
-  // store this group's half of x chunk cs, then reload the registers with x
-  // chunk cs + 1 and weight chunk cw_next.
-  auto mem_phase = [&](int cd, int cs, int cw_next) {
+  // Memory phase of group 0: decode chunk cd's weights (loaded one chunk
+  // ago), hand group 1's half of them over, store this group's half of x
+  // chunk cs, then load x chunk cs + 1 and weight chunk cw_next.
+  auto mem_phase0 = [&](int cd, int cs, int cw_next) {
     decode_all(cd);
+    hand_over();
     store_a(cs & 1);
     load_a(cs + 1, 0, AV / 2);
     load_w(cw_next);
     pin_operands();
   };
+  // Memory phase of group 1: take chunk cd's words over from LDS (written by
+  // group 0 in the previous phase) and decode them, store x chunk cs, load
+  // x chunk cs + 1.
+  auto mem_phase1 = [&](int cd, int cs) {
+    take_over();
+    decode_all(cd);
+    store_a(cs & 1);
+    load_a(cs + 1, 0, AV / 2);
+    pin_operands();
+  };
 
   // Prologue: the block's scales into LDS; x tile 0 complete in buffer 0;
-  // group 0's operands for chunk 0 decoded and its weights of chunk 1 in
-  // flight; group 1 holds chunk 0's weights.  Both hold their half of x
+  // group 0's operands for chunk 0 decoded, group 1's half of chunk 0 handed
+  // over, and weight chunk 1 in flight.  Both groups hold their half of x
   // chunk 1 in registers.
   {
     // 16-byte loads for the whole granules (a load that straddles the end
@@ -770,12 +808,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     }
   }
   load_a(0, 0, AV);
-  load_w(0);
+  if (grp == 0) load_w(0);
   store_a(0);
   load_a(1, 0, AV);
   lds_barrier();                         // scales visible
   if (grp == 0) {
     decode_all(0);
+    hand_over();
     load_w(1);
     pin_operands();
   }
@@ -784,12 +823,12 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     for (int c = 0; c < nchunks; ++c) {
       mfma_phase(c, c + 1);
       lds_barrier();
-      mem_phase(c + 1, c + 1, c + 2);
+      mem_phase0(c + 1, c + 1, c + 2);
       lds_barrier();
     }
   } else {
     for (int c = 0; c < nchunks; ++c) {
-      mem_phase(c, c + 1, c + 1);
+      mem_phase1(c, c + 1);
       lds_barrier();
       mfma_phase(c, c + 2);
       lds_barrier();
