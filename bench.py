@@ -307,7 +307,7 @@ def q1_bench(torch, tq2, G, dev, stream, args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only; --gpus %d is not supported "
+        print("bench.py: the library runs and is measured on one GPU; --gpus %d is not supported "
               "(run with --gpus 1)" % args.gpus, file=sys.stderr)
         return 2
 
