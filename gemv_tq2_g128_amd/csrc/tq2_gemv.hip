@@ -64,6 +64,27 @@ __device__ __forceinline__ void decode_word(uint32_t w, uint32_t magic, half2_t 
   }
 }
 
+// Sum of v over aligned groups of G consecutive lanes (G a power of two, at
+// most 64) with DPP lane moves: xor 1 and 2 (quad permutes), then the 8- and
+// 16-lane mirrors, then the row broadcasts of lanes 15 and 31.  Afterwards
+// lane G - 1 of each group holds the group's sum.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_move<0xB1, 0xF>(v);     // quad_perm [1, 0, 3, 2]
+  if constexpr (G >= 4) v += dpp_move<0x4E, 0xF>(v);     // quad_perm [2, 3, 0, 1]
+  if constexpr (G >= 8) v += dpp_move<0x141, 0xF>(v);    // row_half_mirror
+  if constexpr (G >= 16) v += dpp_move<0x140, 0xF>(v);   // row_mirror
+  if constexpr (G >= 32) v += dpp_move<0x142, 0xA>(v);   // row_bcast15 into rows 1 and 3
+  if constexpr (G >= 64) v += dpp_move<0x143, 0xC>(v);   // row_bcast31 into rows 2 and 3
+  return v;
+}
+
 // Code words per weight row, and the code word of lane unit u (16 weights):
 // TQ2 word u; Q1 half (u & 1) of word u >> 1, moved to the low byte of each
 // half-word so that pair r of the unit sits at bits r and r + 16.
@@ -170,6 +191,13 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
   const int wpr = k >> 4;                       // lane units (16 weights) per row
   const int kb_count = k >> 7;
   const int row0 = blk * OUTS + slot * ROWS;
+  // The output row this thread finishes (if it is its group's last lane),
+  // and its residual, loaded first so that its latency is hidden.
+  const int g = t % G;
+  const int orow = blk * OUTS + t / G;
+  const bool writer = g == G - 1 && orow < n_rows;
+  float rres = 0.f;
+  if (residual && writer) rres = residual[orow];
 
   float part[ROWS];
 #pragma unroll
@@ -206,19 +234,14 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
   const int o = t / G;                          // block row finished by this thread
   const int os = o / ROWS;                      // its slot
   const int orr = o % ROWS;                     // its row inside the slot
-  const int g = t % G;
   constexpr int PER = LPS / G;                  // partials summed by one thread
   float v = 0.f;
 #pragma unroll
   for (int i = 0; i < PER; ++i) v += red[orr][os * LPS + g * PER + i];
-#pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  if (g == 0) {
-    const int row = blk * OUTS + os * ROWS + orr;
-    if (row < n_rows) {
-      if (residual) v = residual[row] + v;
-      out[row] = v;
-    }
+  v = group_sum<G>(v);
+  if (writer) {                                 // orow == blk * OUTS + os * ROWS + orr
+    if (residual) v = rres + v;
+    out[orow] = v;
   }
 }
 
@@ -338,13 +361,10 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
     vg += red[orr][os * LPS + g * PER + i];
     vu += red[orr + HALF][os * LPS + g * PER + i];
   }
-#pragma unroll
-  for (int off = G / 2; off >= 1; off >>= 1) {
-    vg += __shfl_xor(vg, off, 64);
-    vu += __shfl_xor(vu, off, 64);
-  }
+  vg = group_sum<G>(vg);
+  vu = group_sum<G>(vu);
   const int row = blockIdx.x * OUTS + o;
-  if (g == 0 && row < n_rows) out[row] = silu(vg) * vu;
+  if (g == G - 1 && row < n_rows) out[row] = silu(vg) * vu;
 }
 
 template <int ROWS, Fmt F>
