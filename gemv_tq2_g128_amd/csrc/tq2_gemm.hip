@@ -124,6 +124,19 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// x = hi + lo for a pair of f32: hi = binary16(x) (round to nearest even),
+// lo = binary16(x - hi), where x - hi is exact in f32 and comes from one
+// v_fma_mix_f32 per element (hi read as binary16 from the packed pair).
+__device__ __forceinline__ void split_limbs(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const half2_t h = {_Float16(a), _Float16(b)};
+  hi = __builtin_bit_cast(uint32_t, h);
+  float ra, rb;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(hi), "v"(a));
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(hi), "v"(b));
+  const half2_t l = {_Float16(ra), _Float16(rb)};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // Store an MT x NO f32 result tile, staged row-major in LDS with row pitch
 // NO + 4, to out[m0 + r][n0 + c] (plus the residual): THREADS threads walk
 // the tile in whole rows, 16 bytes per lane, so each store instruction
@@ -498,6 +511,249 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
   }
   __syncthreads();
   store_tile<MT, NT, THREADS>(tile, tid, m0, n0, M, N, residual, out);
+}
+
+// ---------------------------------------------------------------------------
+// Skinny variant for M <= 16 with x split into two binary16 limbs (the
+// f32-class path).  At this M the work per weight is tiny, so the kernel is
+// laid out for the weight stream rather than for matrix-core reuse: the
+// block's waves split K, not N.  In pass p wave w owns the slice
+// k in [4096 p + SLICE w, +SLICE), SLICE = 4096 / WAVES.  It loads that slice
+// of x once, one row per 16-byte-per-lane load (whole cache lines), converts
+// it to the hi and lo binary16 limbs, and passes it through a per-wave LDS
+// region into operand fragments that stay in registers.  Meanwhile the code
+// words and scales of the block's 16-column tiles are already in flight
+// (PF tiles ahead); the wave streams them through the fragments with no
+// barrier inside the K loop.  The waves' partial sums of each output meet in
+// LDS once, at the end.
+//
+// PACK (M <= 8): the B operand's 16 columns hold the hi limbs of x rows 0..7
+// and the lo limbs of the same rows, so one MFMA per step covers both limbs
+// and output (m, n) is D[n][m] + D[n][m + 8].  Otherwise (M <= 16) the limbs
+// take one MFMA each.  Lane mapping per 256-wide chunk and MFMA step as in
+// gemm_kernel: the fragment of step s is x[col][64g + 8s .. +7].
+template <int TMAX, int WAVES, bool PACK, bool SWIGLU, Fmt F>
+__global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
+    const float* __restrict__ x, const float* __restrict__ residual, float* __restrict__ out,
+    int M, int N, int K) {
+  constexpr int THREADS = 64 * WAVES;
+  constexpr int PASS_K = 4096;
+  constexpr int SLICE = PASS_K / WAVES;  // k per wave per pass
+  constexpr int CPW = SLICE / kChunk;    // 256-wide chunks per wave
+  constexpr int BITS = int(F);
+  constexpr int QW = 2 * BITS;           // code dwords per lane per chunk
+  constexpr int NMAT = SWIGLU ? 2 : 1;   // weights read per tile (gate, up)
+  constexpr int PF = SWIGLU ? 2 : TMAX;  // tiles whose loads are in flight
+  constexpr int XR = PACK ? 8 : 16;      // x rows staged
+  constexpr int LIMBS = PACK ? 1 : 2;    // MFMAs per step
+  constexpr int LROWS = 2 * XR;          // LDS rows per wave: hi rows, then lo rows
+  constexpr int XS_BYTES = WAVES * LROWS * kLdsRow * 2;
+  constexpr int RED_BYTES = WAVES * TMAX * NMAT * 4 * 64 * 4;
+  static_assert(CPW >= 1 && CPW * kChunk * WAVES == PASS_K, "slice split");
+  typedef uint32_t codes_t[QW];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[XS_BYTES > RED_BYTES ? XS_BYTES : RED_BYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int KB = K >> 7;
+  const int tiles = (N + 15) >> 4;
+  const int tile0 = blockIdx.x * TMAX;
+  const int ntile = min(TMAX, tiles - tile0);
+  _Float16* xs = reinterpret_cast<_Float16*>(smem) + wave * LROWS * kLdsRow;
+
+  // x rows past M, columns past N read as zero.
+  const rsrc_t rx = make_rsrc(x, uint32_t(M) * uint32_t(K) * 4u);
+  const uint32_t row_bytes = uint32_t(K / 8) * uint32_t(BITS);
+  const rsrc_t rc[2] = {make_rsrc(codes, uint32_t(N) * row_bytes),
+                        make_rsrc(SWIGLU ? ucodes : codes, uint32_t(N) * row_bytes)};
+  const rsrc_t rs[2] = {make_rsrc(scales, uint32_t(N) * uint32_t(KB) * 2u),
+                        make_rsrc(SWIGLU ? uscales : scales, uint32_t(N) * uint32_t(KB) * 2u)};
+
+  floatx4_t acc[TMAX][NMAT];             // [tile][gate/up]; both limbs accumulate here
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q) acc[t][q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t magic = 0x64006400u;
+  const int npass = (K + PASS_K - 1) / PASS_K;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int k0 = pass * PASS_K + wave * SLICE;
+    if (k0 >= K) break;                  // wave-uniform: the rest of K is past the end
+    const bool all_live = k0 + SLICE <= K;
+
+    // ---- x slice: row r of chunk h is one 1 KB load (16 bytes per lane) ----
+    float4 xq[CPW][XR];
+#pragma unroll
+    for (int h = 0; h < CPW; ++h)
+#pragma unroll
+      for (int r = 0; r < XR; ++r) {
+        const uint32_t off = (uint32_t(r) * uint32_t(K) + uint32_t(k0 + 256 * h + 4 * lane)) * 4u;
+        xq[h][r] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- weights: tile t's code words and scales, PF tiles in flight -------
+    codes_t cw[PF][NMAT][CPW];
+    _Float16 dr[PF][NMAT][CPW];
+    auto load_tile = [&](int t, codes_t (&c)[NMAT][CPW], _Float16 (&d)[NMAT][CPW]) {
+      const uint32_t n = uint32_t(16 * (tile0 + min(t, ntile - 1)) + col);
+#pragma unroll
+      for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int h = 0; h < CPW; ++h) {
+          const uint32_t kk = uint32_t(k0 + 256 * h + 64 * g);
+          const uint32_t off = n * row_bytes + kk / 8u * uint32_t(BITS);
+          if constexpr (QW == 4) {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc[q], off, 0, 0);
+            c[q][h][0] = v[0]; c[q][h][1] = v[1]; c[q][h][2] = v[2]; c[q][h][3] = v[3];
+          } else {
+            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc[q], off, 0, 0);
+            c[q][h][0] = v[0]; c[q][h][1] = v[1];
+          }
+          d[q][h] = __builtin_bit_cast(
+              _Float16, __builtin_amdgcn_raw_buffer_load_b16(
+                            rs[q], (n * uint32_t(KB) + (kk >> 7)) * 2u, 0, 0));
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < PF; ++t) load_tile(t, cw[t], dr[t]);
+    __builtin_amdgcn_sched_barrier(0);   // weights in flight while x is converted
+
+    // ---- x fragments: hi = binary16(x) (RNE), lo = binary16(x - hi) --------
+    // Lane l converts k = 4l .. 4l+3 of each row into LDS row r (hi) and row
+    // XR + r (lo); each lane then reads its fragments back.  Positions past K
+    // are zeroed (a partial last slice).  A later chunk reuses the region
+    // once the previous chunk's reads have completed.
+    half8_t xf[CPW][8][LIMBS];
+#pragma unroll
+    for (int h = 0; h < CPW; ++h) {
+      if (h > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const bool live = all_live || k0 + 256 * h + 4 * lane < K;
+      const uint32_t keep = live ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int r = 0; r < XR; ++r) {
+        float4 v = xq[h][r];
+        if (!all_live) {                 // wave-uniform
+          v.x = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v.x) & keep);
+          v.y = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v.y) & keep);
+          v.z = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v.z) & keep);
+          v.w = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v.w) & keep);
+        }
+        uint32_t hi[2], lo[2];
+        split_limbs(v.x, v.y, hi[0], lo[0]);
+        split_limbs(v.z, v.w, hi[1], lo[1]);
+        *reinterpret_cast<u32x2_t*>(&xs[r * kLdsRow + 4 * lane]) = u32x2_t{hi[0], hi[1]};
+        *reinterpret_cast<u32x2_t*>(&xs[(XR + r) * kLdsRow + 4 * lane]) = u32x2_t{lo[0], lo[1]};
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int l = 0; l < LIMBS; ++l)
+          xf[h][st][l] = *reinterpret_cast<const half8_t*>(&xs[(16 * l + col) * kLdsRow + 64 * g + 8 * st]);
+    }
+
+    // ---- stream the tiles ----------------------------------------------------
+    auto compute = [&](int t, const codes_t (&c)[NMAT][CPW], const _Float16 (&d)[NMAT][CPW]) {
+#pragma unroll
+      for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+        for (int h = 0; h < CPW; ++h) {
+          const bool live = all_live || k0 + 256 * h + 64 * g < K;
+          const _Float16 dd = live ? d[q][h] : _Float16(0.0f);
+          uint32_t cf[QW];
+          half2_t d2;
+          if constexpr (F == Fmt::kQ1) {
+            const uint32_t db = __builtin_bit_cast(uint16_t, dd);
+            d2 = __builtin_bit_cast(half2_t, q1_dabs2(db));
+            const uint32_t fold = q1_fold(db);
+#pragma unroll
+            for (int i = 0; i < QW; ++i) cf[i] = c[q][h][i] ^ fold;
+          } else {
+            d2 = half2_t{dd, dd};
+#pragma unroll
+            for (int i = 0; i < QW; ++i) cf[i] = c[q][h][i];
+          }
+#pragma unroll
+          for (int st = 0; st < 8; ++st) {
+            half8_t b;
+            if constexpr (F == Fmt::kQ1) {
+              b = decode_step_q1(cf[st >> 2], 4 * (st & 3), __builtin_bit_cast(uint32_t, d2));
+            } else {
+              uint32_t w = cf[st >> 1];
+              if (st & 1) w >>= 8;
+              b = decode_step(w, d2, magic);
+            }
+#pragma unroll
+            for (int l = 0; l < LIMBS; ++l)
+              acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, xf[h][st][l], acc[t][q], 0, 0, 0);
+          }
+        }
+    };
+    // Every block computes TMAX tiles; in the last block the tiles past the
+    // end repeat its last tile (results not stored), so that no branch
+    // splits the load stream.
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const int slot = t % PF;
+      compute(t, cw[slot], dr[slot]);
+      if (t + PF < TMAX) load_tile(t + PF, cw[slot], dr[slot]);
+    }
+  }
+
+  // ---- the waves' partial sums meet in LDS -----------------------------------
+  // acc holds D[n = 4g + e][j = col] of each tile (the weight is the MFMA's
+  // row operand).  red[wave][tile][gate/up][e][lane].
+  __syncthreads();                       // every wave is done with its x region
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        red[(((wave * TMAX + t) * NMAT + q) * 4 + e) * 64 + lane] = acc[t][q][e];
+  __syncthreads();
+  // Thread o of the block finishes output (m, tile t, column c): consecutive
+  // threads take consecutive columns of one row, so the stores coalesce.
+  const int cols = ntile * 16;
+  const int rows = min(M, XR);
+  for (int o = tid; o < rows * cols; o += THREADS) {
+    const int m = o / cols;
+    const int rem = o - m * cols;
+    const int t = rem >> 4;
+    const int c = rem & 15;
+    const int n = 16 * (tile0 + t) + c;
+    if (n >= N) continue;
+    const int ln = m + 16 * (c >> 2);
+    const int e = c & 3;
+    float v[NMAT];
+#pragma unroll
+    for (int q = 0; q < NMAT; ++q) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        const float* rw = &red[(((w * TMAX + t) * NMAT + q) * 4 + e) * 64];
+        sum += PACK ? rw[ln] + rw[ln + 8] : rw[ln];
+      }
+      v[q] = sum;
+    }
+    const size_t oi = size_t(m) * N + n;
+    float r;
+    if constexpr (SWIGLU) {
+      r = silu(v[0]) * v[1];
+    } else {
+      r = v[0];
+      if (residual) r = residual[oi] + r;
+    }
+    out[oi] = r;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -937,17 +1193,54 @@ hipError_t launch_tile(const uint8_t* soa, const uint8_t* up, const float* x,
   return hipGetLastError();
 }
 
+// Skinny kernel: TMAX 16-column tiles per block, so that about one block
+// per CU covers N (at most 4 tiles per block; more blocks beyond that).
+template <int TMAX, bool SWIGLU, Fmt F>
+hipError_t launch_skinny(const uint8_t* soa, const uint8_t* up, const float* x,
+                         const float* residual, float* out, int64_t m, int64_t n, int64_t k,
+                         hipStream_t stream) {
+  const int64_t tiles = (n + 15) / 16;
+  const int64_t blocks = (tiles + TMAX - 1) / TMAX;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const size_t so = scales_offset(F, n, k);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  // M <= 8 packs both limbs into one MFMA column set and stages 8 x rows per
+  // wave, so 16 waves (one 256-wide chunk each) fit the LDS; M <= 16 uses 8.
+  if (m <= 8)
+    hipLaunchKernelGGL((gemm_skinny_kernel<TMAX, 16, true, SWIGLU, F>), grid, dim3(1024), 0,
+                       stream, soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m),
+                       int(n), int(k));
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<TMAX, 8, false, SWIGLU, F>), grid, dim3(512), 0,
+                       stream, soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m),
+                       int(n), int(k));
+  return hipGetLastError();
+}
+
+template <bool SWIGLU, Fmt F>
+hipError_t dispatch_skinny(const uint8_t* soa, const uint8_t* up, const float* x,
+                           const float* residual, float* out, int64_t m, int64_t n, int64_t k,
+                           hipStream_t stream) {
+  constexpr int64_t kCus = 256;
+  const int64_t tiles = (n + 15) / 16;
+  const int64_t want = (tiles + kCus - 1) / kCus;
+  const int tpb = int(want < 4 ? want : 4);
+  if (tpb <= 1) return launch_skinny<1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+  if (tpb == 2) return launch_skinny<2, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+  if (tpb == 3) return launch_skinny<3, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+  return launch_skinny<4, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+}
+
 // Kernel choice by path and M (shared by the plain and the SwiGLU forms).
 template <bool SWIGLU, Fmt F>
 hipError_t dispatch(int path, const uint8_t* soa, const uint8_t* up, const float* x,
                     const float* residual, float* out, int64_t m, int64_t n, int64_t k,
                     hipStream_t stream) {
   if (path == 1) {
-    // Split-binary16 (f32-class) kernel: 16-row tiles up to M = 16, 64-row
-    // tiles beyond (tq2_gemm_precise), so each weight is decoded once per 64
-    // rows of x.
-    if (m <= 16)
-      return launch_tile<16, 16, 4, 2, 2, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+    // Split-binary16 (f32-class) kernels: the skinny kernel up to M = 16,
+    // 64-row tiles beyond (tq2_gemm_precise), so each weight is decoded once
+    // per 64 rows of x.
+    if (m <= 16) return dispatch_skinny<SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
     return launch_tile<64, 16, 4, 2, 2, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
   }
   if (m <= 32)

@@ -15,6 +15,8 @@
 // Latency.  The code words and scales of all ROWS rows are loaded with
 // clamped, branch-free addresses before any arithmetic, so one block keeps
 // ROWS loads per lane in flight instead of paying the HBM latency per row.
+// The lane's x values are loaded before them: loads complete in issue order,
+// so row r's arithmetic starts as soon as row r's weights have arrived.
 //
 // Arithmetic (f32 products and sums, weights exact).  One AND-OR puts two
 // codes of the word into the mantissas of a binary16 pair 1024 + 4^f c (the
@@ -121,24 +123,8 @@ __device__ __forceinline__ float dot16_q1(uint32_t w, const float (&xv)[16]) {
   return -(s0 + s1);                            // (-1)^b = -(2b - 1)
 }
 
-// Load ROWS code words and scales of lane unit wc (16 weights), and the 16 x
-// values of it.
-template <int ROWS, Fmt F>
-__device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
-                                             const uint16_t* __restrict__ scales,
-                                             const float* __restrict__ x, int row0, int n_rows,
-                                             int k, int kb_count, int wc, uint32_t (&cw)[ROWS],
-                                             uint32_t (&db)[ROWS], float (&xv)[16]) {
-  const unsigned uwc = unsigned(wc);            // lane offset: 32-bit, base pointer uniform
-  const int wrow = words_per_row<F>(k);
-#pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    const int row = min(row0 + r, n_rows - 1);
-    const uint32_t* crow = codes + size_t(row) * wrow;
-    const uint16_t* srow = scales + size_t(row) * kb_count;
-    cw[r] = unit_word<F>(crow, uwc);
-    db[r] = srow[uwc >> 3];
-  }
+// The 16 x values of lane unit wc.
+__device__ __forceinline__ void load_x16(const float* __restrict__ x, int wc, float (&xv)[16]) {
   const float4* xp = reinterpret_cast<const float4*>(x + 16 * wc);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -147,6 +133,30 @@ __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
     xv[4 * i + 1] = q.y;
     xv[4 * i + 2] = q.z;
     xv[4 * i + 3] = q.w;
+  }
+}
+
+// Load the 16 x values of lane unit wc (16 weights), then ROWS code words
+// and scales of it.  Vector loads return in issue order, so the x loads (L2
+// hits) go first: the arithmetic of row 0 then waits only for row 0's
+// weights, and each later row's arithmetic overlaps the arrival of the rest.
+template <int ROWS, Fmt F>
+__device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
+                                             const uint16_t* __restrict__ scales,
+                                             const float* __restrict__ x, int row0, int n_rows,
+                                             int k, int kb_count, int wc, uint32_t (&cw)[ROWS],
+                                             uint32_t (&db)[ROWS], float (&xv)[16]) {
+  const unsigned uwc = unsigned(wc);            // lane offset: 32-bit, base pointer uniform
+  const int wrow = words_per_row<F>(k);
+  load_x16(x, wc, xv);
+  __builtin_amdgcn_sched_barrier(0);            // keep the x loads first
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const int row = min(row0 + r, n_rows - 1);
+    const uint32_t* crow = codes + size_t(row) * wrow;
+    const uint16_t* srow = scales + size_t(row) * kb_count;
+    cw[r] = unit_word<F>(crow, uwc);
+    db[r] = srow[uwc >> 3];
   }
 }
 
@@ -315,6 +325,8 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   // Rows 0..HALF-1 from the gate weight, HALF..ROWS-1 from the up weight.
   auto load = [&](int wc) {
     const unsigned uwc = unsigned(wc);
+    load_x16(x, wc, xv);                        // x first, as in load_segment
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const int row = min(out0 + (r % HALF), n_rows - 1);
@@ -322,15 +334,6 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
       const uint16_t* srow = (r < HALF ? gscales : uscales) + size_t(row) * kb_count;
       cw[r] = unit_word<F>(crow, uwc);
       db[r] = srow[uwc >> 3];
-    }
-    const float4* xp = reinterpret_cast<const float4*>(x + 16 * wc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 q = xp[i];
-      xv[4 * i] = q.x;
-      xv[4 * i + 1] = q.y;
-      xv[4 * i + 2] = q.z;
-      xv[4 * i + 3] = q.w;
     }
   };
   if constexpr (ONE_SEG) {
