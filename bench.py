@@ -40,6 +40,8 @@ def parse():
                    help="skip the batched decode GEMV (16 weights per call)")
     p.add_argument("--no-chain", action="store_true",
                    help="skip the 100-layer M=1536 chain (config 5)")
+    p.add_argument("--no-small-batch", action="store_true",
+                   help="skip the small-batch prefill GEMM lines (M = 7, 8, 9, 100; K=4096 -> N=11008)")
     p.add_argument("--no-swiglu", action="store_true",
                    help="skip the fused gate/up + SwiGLU lines (K=4096 -> N=11008)")
     p.add_argument("--no-q1", action="store_true",
@@ -244,6 +246,48 @@ def swiglu_bench(torch, tq2, G, dev, stream, args):
     }
 
 
+def small_batch_bench(torch, tq2, G, dev, stream, args):
+    """Small-batch prefill GEMM, K = 4096 -> N = 11008 (half-zero codes,
+    d ~ U[0.005, 0.05]) at the workload's M = 7, 8, 9 and 100; the weight is
+    rotated over copies larger than the Infinity Cache, as for the GEMV.
+    Reported per M: time per call, algorithmic bytes (weight + x + out) per
+    second and the fraction of the HBM peak, and the path taken."""
+    import numpy as np
+    out_lines = {}
+    c = G.config3(100)
+    n, k = c["n"], c["k"]
+    soa = tq2.reformat_aos_to_soa(torch.from_numpy(c["aos"]).to(dev), n, k)
+    sb = tq2.soa_bytes(n, k)
+    pool = max(1, int(math.ceil(args.pool_mib * 2 ** 20 / sb)))
+    wpool = soa.repeat(pool)
+    base = wpool.data_ptr()
+    for m in (7, 8, 9, 100):
+        # config3(m)'s x is the first m rows of the same 100-row draw
+        x = torch.from_numpy(np.ascontiguousarray(c["x"][:m])).to(dev)
+        out = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+        def call(i, x=x, out=out, m=m):
+            st = tq2.gemm_ptr(base + (i % pool) * sb, x.data_ptr(), 0, out.data_ptr(), m, n, k,
+                              torch.cuda.current_stream(dev).cuda_stream)
+            if st != 0:
+                raise RuntimeError("tq2_gemm failed: %s" % tq2.status_string(st))
+
+        g = capture(torch, stream, call, pool)
+        time_graph(torch, g, 1, stream)
+        reps = max(1, int(math.ceil(args.steps / 8 / pool)))
+        ms, _ = time_graph(torch, g, reps, stream)
+        us = ms * 1e3 / (reps * pool)
+        nbytes = n * (k // 128) * 34 + 4 * m * k + 4 * m * n
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out_lines["m%d" % m] = {"us_per_call": round(us, 3), "gbs": round(gbs, 2),
+                                "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 2),
+                                "path": tq2.gemm_path(m, n, k), "calls": reps * pool}
+        del g
+    del wpool
+    return {"gemm_small_batch_k4096_n11008": out_lines}
+
+
 def q1_bench(torch, tq2, G, dev, stream, args):
     """Q1_g128 (1-bit) sibling format on the same shapes as the TQ2 lines:
     decode GEMV M=1, K=N=4096 with residual (weight copies rotated past the
@@ -444,6 +488,9 @@ def main():
             "path": tq2.gemm_path(m4, n4, k4), "calls": reps * per_graph,
             "traffic": measured_traffic("gemm_traffic_bytes_per_launch",
                                         "gemv_tq2_g128_amd/csrc/tq2_gemm.hip")}
+
+    if not args.no_small_batch:
+        result.update(small_batch_bench(torch, tq2, G, dev, stream, args))
 
     if not args.no_swiglu:
         result.update(swiglu_bench(torch, tq2, G, dev, stream, args))
