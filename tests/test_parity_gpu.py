@@ -192,6 +192,26 @@ def test_gemm_shapes(tq2, m, n, k):
     assert_case(tq2, c2)
 
 
+# The skinny kernel (M <= 16): every tiles-per-block instantiation (N up to
+# 16 400, so the grid also exceeds 256 blocks), a ragged last block, one to
+# four passes over K with partial last slices and chunks, both sides of the
+# M = 8 packing limit, and the in-place residual.
+SKINNY_SHAPES = [(8, 1, 128), (2, 300, 12416), (5, 4100, 4224), (9, 33, 4096),
+                 (12, 8200, 2176), (16, 12290, 8320), (7, 16400, 1024), (16, 4096, 4096)]
+
+
+@pytest.mark.parametrize("m,n,k", SKINNY_SHAPES)
+def test_skinny_shapes(tq2, m, n, k):
+    assert tq2.gemm_path(m, n, k) == 1
+    c = G.random_case(2500 + m + n + k, m, n, k, residual=True)
+    assert_case(tq2, c)
+
+
+def test_skinny_inplace_residual(tq2):
+    c = G.random_case(2601, 6, 4100, 4224, residual=True)
+    assert_case(tq2, c, inplace=True)
+
+
 # ---------------------------------------------------------------------------
 # Edge values and degenerate cases.
 # ---------------------------------------------------------------------------
@@ -387,7 +407,8 @@ def test_swiglu_decode_shapes(tq2, n, k):
 
 # M = 2..16: split-binary16 kernel; 17..128: 16-column-group kernels; > 128
 # with K <= 12288: the ping-pong kernel; K > 12288: the wide-tile kernel.
-SWIGLU_GEMM_SHAPES = [(2, 17, 128), (9, 100, 384), (16, 257, 1024), (17, 33, 256),
+SWIGLU_GEMM_SHAPES = [(2, 17, 128), (9, 100, 384), (16, 257, 1024), (5, 4100, 4224),
+                      (12, 8200, 2176), (17, 33, 256),
                       (40, 130, 640), (64, 96, 384), (100, 191, 1024), (129, 191, 384),
                       (200, 97, 768), (300, 1000, 1152), (150, 50, 12416)]
 

@@ -115,7 +115,8 @@ def test_q1_decode_workload(tq2):
     assert_q1(tq2, dict(G.q1_decode(True), gemv=True), inplace=True)
 
 
-Q1_GEMM_SHAPES = [(2, 17, 128), (9, 100, 384), (16, 257, 1024), (17, 200, 384), (33, 100, 256),
+Q1_GEMM_SHAPES = [(2, 17, 128), (9, 100, 384), (16, 257, 1024), (5, 4100, 4224), (12, 8200, 2176),
+                  (17, 200, 384), (33, 100, 256),
                   (64, 129, 384), (100, 300, 1024), (128, 64, 256), (129, 191, 384),
                   (200, 385, 768), (300, 1000, 1152), (150, 50, 12416)]
 
@@ -149,8 +150,8 @@ def test_q1_special_bits_and_scales(tq2, m):
         assert_q1(tq2, c)
 
 
-SWIGLU_Q1 = [(1, 300, 4096), (1, 77, 12288), (9, 100, 384), (40, 130, 640), (200, 97, 768),
-             (129, 191, 1024)]
+SWIGLU_Q1 = [(1, 300, 4096), (1, 77, 12288), (9, 100, 384), (5, 4100, 4224), (40, 130, 640),
+             (200, 97, 768), (129, 191, 1024)]
 
 
 @pytest.mark.parametrize("m,n,k", SWIGLU_Q1)
