@@ -46,6 +46,8 @@ def parse():
                    help="skip the fused gate/up + SwiGLU lines (K=4096 -> N=11008)")
     p.add_argument("--no-q1", action="store_true",
                    help="skip the Q1_g128 (1-bit) decode GEMV and M=1536 GEMM lines")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the decode GEMV size sweep (N = K = 4096, 8192, 16384)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device-to-device copy of this size (MiB) so a "
                         "counter run can scale FETCH_SIZE / WRITE_SIZE against known bytes")
@@ -72,6 +74,30 @@ def measured_traffic(key, source):
             if fields.get("kernel_source_sha256") == digest:
                 return int(fields[key])
     return None
+
+
+def run_environment(torch):
+    """Device, HIP runtime and ROCm version, and the GFX clock limits that
+    amd-smi reports (None where the tool is not available)."""
+    import re
+    import subprocess
+    env = {"device": torch.cuda.get_device_name(0), "hip_runtime": torch.version.hip,
+           "rocm": None, "gfx_clock_mhz_max": None, "gfx_clock_mhz_min": None}
+    try:
+        txt = subprocess.run(["amd-smi", "version"], capture_output=True, text=True,
+                             timeout=20).stdout
+        m = re.search(r"ROCm version:\s*([0-9.]+)", txt)
+        env["rocm"] = m.group(1) if m else None
+        txt = subprocess.run(["amd-smi", "metric", "-c", "-g", "0"], capture_output=True,
+                             text=True, timeout=20).stdout
+        blk = txt.split("GFX_0:", 1)[1] if "GFX_0:" in txt else ""
+        mx = re.search(r"MAX_CLK:\s*([0-9]+)", blk)
+        mn = re.search(r"MIN_CLK:\s*([0-9]+)", blk)
+        env["gfx_clock_mhz_max"] = int(mx.group(1)) if mx else None
+        env["gfx_clock_mhz_min"] = int(mn.group(1)) if mn else None
+    except (OSError, subprocess.SubprocessError, IndexError):
+        pass
+    return env
 
 
 def gemv_bytes(n, k, residual):
@@ -244,6 +270,49 @@ def swiglu_bench(torch, tq2, G, dev, stream, args):
             "peak_tflops": F16_MFMA_PEAK_TFLOPS, "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
             "path": tq2.gemm_path(m, n, k), "calls": repm * per_graph},
     }
+
+
+def gemv_sweep(torch, tq2, G, dev, stream, args):
+    """Decode GEMV with residual at N = K = 4096, 8192 and 16384 (config 2's
+    code and scale distributions, seed 20 + N/4096), each weight rotated over
+    copies larger than the Infinity Cache and replayed back to back from a HIP
+    graph.  The fixed per-launch cost weighs less as the weight grows."""
+    import numpy as np
+    lines = {}
+    for size in (4096, 8192, 16384):
+        n = k = size
+        rng = np.random.default_rng(20 + size // 4096)
+        aos = torch.from_numpy(G.make_weight(rng, n, k)).to(dev)
+        x = torch.from_numpy(G.make_activations(rng, 1, k)).to(dev).reshape(-1)
+        res = torch.from_numpy(rng.standard_normal(n, dtype=np.float32)).to(dev)
+        soa = tq2.reformat_aos_to_soa(aos, n, k)
+        del aos
+        sb = tq2.soa_bytes(n, k)
+        pool = max(2, int(math.ceil(args.pool_mib * 2 ** 20 / sb)))
+        buf = soa.repeat(pool)
+        del soa
+        base = buf.data_ptr()
+        out = torch.empty(n, dtype=torch.float32, device=dev)
+
+        def call(i):
+            st = tq2.gemv_ptr(base + (i % pool) * sb, x.data_ptr(), res.data_ptr(), out.data_ptr(),
+                              n, k, torch.cuda.current_stream(dev).cuda_stream)
+            if st != 0:
+                raise RuntimeError("tq2_gemv failed: %s" % tq2.status_string(st))
+
+        g = capture(torch, stream, call, pool)
+        time_graph(torch, g, 1, stream)
+        reps = max(1, int(math.ceil(args.steps / 4 / pool)))
+        ms, _ = time_graph(torch, g, reps, stream)
+        us = ms * 1e3 / (reps * pool)
+        nbytes = gemv_bytes(n, k, True)
+        del g, buf
+        lines["n%d_k%d" % (n, k)] = {
+            "us_per_call": round(us, 3), "bytes_per_call": nbytes,
+            "gbs": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "copies_rotated": pool, "calls": reps * pool}
+    return {"gemv_size_sweep_residual": lines}
 
 
 def small_batch_bench(torch, tq2, G, dev, stream, args):
@@ -489,6 +558,9 @@ def main():
             "traffic": measured_traffic("gemm_traffic_bytes_per_launch",
                                         "gemv_tq2_g128_amd/csrc/tq2_gemm.hip")}
 
+    if not args.no_sweep:
+        result.update(gemv_sweep(torch, tq2, G, dev, stream, args))
+
     if not args.no_small_batch:
         result.update(small_batch_bench(torch, tq2, G, dev, stream, args))
 
@@ -512,6 +584,8 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+
+    result["environment"] = run_environment(torch)
 
     print(json.dumps(result), flush=True)
     return 0
