@@ -137,6 +137,31 @@ __device__ __forceinline__ void split_limbs(float a, float b, uint32_t& hi, uint
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
+// Power-of-two prescale of x for the two-limb (hi + lo) paths: 2^e takes a
+// largest |x| of mx into [2^14, 2^15), so that hi and lo stay clear of
+// binary16's subnormal range whatever the magnitude of x (the scaling is
+// exact, and the sums are scaled back by 2^-e).  mx = 0 gives e = 15.
+__device__ __forceinline__ int prescale_exponent(float mx) {
+  return 15 - __builtin_amdgcn_frexp_expf(mx);
+}
+
+// Largest value over the wave (v >= 0): DPP moves (quad permutes, the 8- and
+// 16-lane mirrors, the row broadcasts of lanes 15 and 31) leave it in lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = fmaxf(v, dpp_move<0xB1, 0xF>(v));
+  v = fmaxf(v, dpp_move<0x4E, 0xF>(v));
+  v = fmaxf(v, dpp_move<0x141, 0xF>(v));
+  v = fmaxf(v, dpp_move<0x140, 0xF>(v));
+  v = fmaxf(v, dpp_move<0x142, 0xA>(v));
+  v = fmaxf(v, dpp_move<0x143, 0xC>(v));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // Store an MT x NO f32 result tile, staged row-major in LDS with row pitch
 // NO + 4, to out[m0 + r][n0 + c] (plus the residual): THREADS threads walk
 // the tile in whole rows, 16 bytes per lane, so each store instruction
@@ -265,13 +290,49 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
       areg[i] = __builtin_bit_cast(float4, v);
     }
   };
-  auto store_a = [&](int buf, const float4 (&areg)[AV]) {
+  // LIMBS = 2: the rows a wave stages (wave w stages rows w + THREADS/64 i)
+  // are scaled by 2^xexp[c & 1][w] in chunk c before the split into hi and
+  // lo.  The wave keeps a running exponent: the prescale_exponent of the
+  // largest |x| it has staged so far (chunks of zeros leave it alone), which
+  // can only fall from chunk to chunk.  The computing lanes bring their sums
+  // of a row to the chunk's exponent of that row before its MFMAs (an exact
+  // power-of-two rescale) and scale the finished sums back at the end.
+  // Positions past K in a partial last chunk hold the next row's x; they are
+  // zeroed, so that the scaling cannot take them past the binary16 range
+  // (their weights are zero, and Inf * 0 would not be).
+  constexpr int SW = THREADS / 64;       // staging waves; row r is staged by wave r % SW
+  __shared__ int xexp[2][LIMBS == 2 ? SW : 1];
+  int erun = 1 << 20;
+  auto store_a = [&](int c, int buf, const float4 (&areg)[AV]) {
+    float4 va[AV];
+#pragma unroll
+    for (int i = 0; i < AV; ++i) va[i] = areg[i];
+    if constexpr (LIMBS == 2) {
+      float mh = 0.f;
+#pragma unroll
+      for (int i = 0; i < AV; ++i) {
+        const int c4 = (tid + THREADS * i) & 63;
+        if (c * kChunk + 4 * c4 >= K) va[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        mh = fmaxf(fmaxf(mh, fmaxf(fabsf(va[i].x), fabsf(va[i].y))),
+                   fmaxf(fabsf(va[i].z), fabsf(va[i].w)));
+      }
+      const float mr = wave_max_nonneg(mh);
+      if (mr > 0.f) erun = min(erun, prescale_exponent(mr));   // a zero chunk says nothing
+      if (lane == 0) xexp[buf][wave] = erun;
+#pragma unroll
+      for (int i = 0; i < AV; ++i) {
+        va[i].x = __builtin_amdgcn_ldexpf(va[i].x, erun);
+        va[i].y = __builtin_amdgcn_ldexpf(va[i].y, erun);
+        va[i].z = __builtin_amdgcn_ldexpf(va[i].z, erun);
+        va[i].w = __builtin_amdgcn_ldexpf(va[i].w, erun);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
       const int f = tid + THREADS * i;
       const int r = f >> 6;
       const int c4 = f & 63;
-      const float4 v = areg[i];
+      const float4 v = va[i];
       half4_t h = {_Float16(v.x), _Float16(v.y), _Float16(v.z), _Float16(v.w)};
       *reinterpret_cast<half4_t*>(&As[buf][0][r][4 * c4]) = h;
       if constexpr (LIMBS == 2) {
@@ -363,7 +424,24 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
     }
   };
 
+  int ecur[RT];                          // LIMBS = 2: exponent of acc[i][.]'s x row
+#pragma unroll
+  for (int i = 0; i < RT; ++i) ecur[i] = 0;
   auto compute = [&](int c, int buf, const codes_t (&cw_raw)[CG], const _Float16 (&dsc)[CG]) {
+    if constexpr (LIMBS == 2) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const int en = xexp[buf][(i * 16 + col) % SW];
+        const int dl = en - ecur[i];
+        ecur[i] = en;
+        if (dl != 0) {                   // skipped by the wave once no exponent moves
+#pragma unroll
+          for (int j = 0; j < CG; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_amdgcn_ldexpf(acc[i][j][e], dl);
+        }
+      }
+    }
     // binary16 pair (d, d), or (0, 0) where k runs past K in the last chunk
     // (Q1: the |d| pair, and the words folded by the sign of d).
     const bool live = c * kChunk + 64 * g < K;
@@ -430,7 +508,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
   // issues loads), so every pass issues the same loads in the same place and
   // the wait counts the compiler derives hold on every path through the loop.
   auto iteration = [&](int c, codes_t (&cw)[CG], _Float16 (&dsc)[CG]) {
-    if (c + 1 >= 0 && c + 1 < nchunks) store_a((c + 1) & 1, areg);
+    if (c + 1 >= 0 && c + 1 < nchunks) store_a(c + 1, (c + 1) & 1, areg);
     load_a(c + 2, areg);
     if (c >= 0 && c < nchunks) compute(c, c & 1, cw, dsc);
     load_w(c + 2, cw, dsc);
@@ -439,6 +517,15 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
   for (int c = -2; c < nchunks; c += 2) {
     iteration(c, cw0, dr0);
     iteration(c + 1, cw1, dr1);
+  }
+  if constexpr (LIMBS == 2) {
+    // acc[i][.] holds sums of x row i * 16 + col times 2^ecur[i].
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CG; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_amdgcn_ldexpf(acc[i][j][e], -ecur[i]);
   }
 
   // ---- K-split reduction: the wk = 1 waves hand their sums to wk = 0 -----
@@ -582,6 +669,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 
   const uint32_t magic = 0x64006400u;
   const int npass = (K + PASS_K - 1) / PASS_K;
+  int e_acc = 0;                         // acc holds the sums times 2^e_acc
   for (int pass = 0; pass < npass; ++pass) {
     const int k0 = pass * PASS_K + wave * SLICE;
     if (k0 >= K) break;                  // wave-uniform: the rest of K is past the end
@@ -625,11 +713,36 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     for (int t = 0; t < PF; ++t) load_tile(t, cw[t], dr[t]);
     __builtin_amdgcn_sched_barrier(0);   // weights in flight while x is converted
 
-    // ---- x fragments: hi = binary16(x) (RNE), lo = binary16(x - hi) --------
+    // ---- x fragments: hi = binary16(x 2^e) (RNE), lo = binary16(x 2^e - hi) --
+    // Positions past K are zeroed (a partial last slice).  One power of two
+    // 2^e per wave and pass (prescale_exponent of the slice's largest |x|
+    // over all rows) scales x before the split; acc is kept at the scale of
+    // the current pass and brought to it from the previous pass's.
+    float mx = 0.f;
+#pragma unroll
+    for (int h = 0; h < CPW; ++h) {
+      const bool live = all_live || k0 + 256 * h + 4 * lane < K;
+      float mh = 0.f;
+#pragma unroll
+      for (int r = 0; r < XR; ++r) {
+        const float4 v = xq[h][r];
+        mh = fmaxf(fmaxf(mh, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+      }
+      mx = fmaxf(mx, live ? mh : 0.f);
+    }
+    const int e = prescale_exponent(wave_max_nonneg(mx));
+    if (pass > 0) {                      // acc from the previous pass's scale to this one's
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+        for (int q = 0; q < NMAT; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][q][i] = __builtin_amdgcn_ldexpf(acc[t][q][i], e - e_acc);
+    }
+    e_acc = e;
     // Lane l converts k = 4l .. 4l+3 of each row into LDS row r (hi) and row
-    // XR + r (lo); each lane then reads its fragments back.  Positions past K
-    // are zeroed (a partial last slice).  A later chunk reuses the region
-    // once the previous chunk's reads have completed.
+    // XR + r (lo); each lane then reads its fragments back.  A later chunk
+    // reuses the region once the previous chunk's reads have completed.
     half8_t xf[CPW][8][LIMBS];
 #pragma unroll
     for (int h = 0; h < CPW; ++h) {
@@ -646,8 +759,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
           v.w = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v.w) & keep);
         }
         uint32_t hi[2], lo[2];
-        split_limbs(v.x, v.y, hi[0], lo[0]);
-        split_limbs(v.z, v.w, hi[1], lo[1]);
+        split_limbs(__builtin_amdgcn_ldexpf(v.x, e), __builtin_amdgcn_ldexpf(v.y, e), hi[0], lo[0]);
+        split_limbs(__builtin_amdgcn_ldexpf(v.z, e), __builtin_amdgcn_ldexpf(v.w, e), hi[1], lo[1]);
         *reinterpret_cast<u32x2_t*>(&xs[r * kLdsRow + 4 * lane]) = u32x2_t{hi[0], hi[1]};
         *reinterpret_cast<u32x2_t*>(&xs[(XR + r) * kLdsRow + 4 * lane]) = u32x2_t{lo[0], lo[1]};
       }
@@ -718,7 +831,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     for (int q = 0; q < NMAT; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        red[(((wave * TMAX + t) * NMAT + q) * 4 + e) * 64 + lane] = acc[t][q][e];
+        red[(((wave * TMAX + t) * NMAT + q) * 4 + e) * 64 + lane] =
+            __builtin_amdgcn_ldexpf(acc[t][q][e], -e_acc);
   __syncthreads();
   // Thread o of the block finishes output (m, tile t, column c): consecutive
   // threads take consecutive columns of one row, so the stores coalesce.

@@ -123,9 +123,12 @@ int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream);
  * same aliasing rules as tq2_gemv.  The kernel is picked by tq2_gemm_path:
  *   0: M == 1, the GEMV above;
  *   1: 2 <= M <= 16: matrix-core GEMM with x split into two binary16 parts
- *      (x = hi + lo), error within 1e-5 * sum|x w| for |x| <= 65504 (the lo
- *      part's absolute resolution is 2^-24, so the bound can fail only for
- *      rows whose |x| stays below about 3e-3);
+ *      (x = hi + lo), error within 1e-5 * sum|x w| at any magnitude of x:
+ *      each wave scales its 4096-wide K slice of x by a power of two before
+ *      the split so that both parts stay normal binary16, and scales the sums
+ *      back (exact); an element more than 2^17 times smaller than the largest
+ *      |x| of its slice (over the rows the wave holds) keeps an absolute error
+ *      below 2^-39 of that largest |x|;
  *   2: M > 16: matrix-core GEMM with x rounded to binary16 and weights staged
  *      as exact binary16 code * d (oxibonsai-kernels 0.1.5, pipelines.rs,
  *      fields `gemm_tq2_g128_v9_simdgroup` / `gemm_tq2_g128_v10_simdgroup`:
@@ -139,8 +142,10 @@ int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
 /* tq2_gemm with f32-class accuracy at every M: the split-binary16 matrix-core
  * kernel of path 1 (x = hi + lo, both parts against the same exact binary16
  * weight, f32 accumulation) for every M >= 2, and the GEMV for M == 1; error
- * within 1e-5 * sum|x w| for |x| <= 65504 (same small-|x| caveat as path 1),
- * at about twice path 2's matrix-core work for M > 16.  The pages stage both operands as binary16 for large M
+ * within 1e-5 * sum|x w| at any magnitude of x (for M > 16 the power of two
+ * is kept per group of x rows and 256-wide K chunk, falling as larger values
+ * arrive, with the sums rescaled to it), at about twice path 2's matrix-core
+ * work for M > 16.  The pages stage both operands as binary16 for large M
  * (pipelines.rs, fields `gemm_tq2_g128_v9_simdgroup` /
  * `gemm_tq2_g128_v10_simdgroup`); this is the variant for callers that need
  * the f32 path's accuracy (their `gemm_tq2_g128_v7` / `_v8_tiled`).  Same

@@ -251,6 +251,65 @@ def test_large_activations_f16_range(tq2):
     assert_case(tq2, c)
 
 
+# The split-binary16 paths (M <= 16, and tq2_gemm_precise at any M) scale x
+# by a power of two before the split (per wave and K pass in the skinny
+# kernel, per x row in the tile kernel), so the 1e-5 tolerance holds at any
+# magnitude of x: without it the lo limb of |x| below about 3e-3 falls into
+# binary16's subnormal range.
+@pytest.mark.parametrize("m", [1, 5, 8, 13, 40])
+@pytest.mark.parametrize("scale", [1e-6, 2e-8, 3e4])
+def test_split_paths_x_magnitudes(tq2, m, scale):
+    c = G.random_case(8800 + m, m, 300, 1280, residual=True)
+    c["x"] = (c["x"] * np.float32(scale)).astype(np.float32)
+    c["residual"] = (c["residual"] * np.float32(scale)).astype(np.float32)
+    c["name"] = "x_scale_%g_m%d" % (scale, m)
+    if m <= 16:
+        assert_case(tq2, c)                      # path 1 (or the GEMV at M = 1)
+    assert_case(tq2, c, precise=True)
+
+
+@pytest.mark.parametrize("m", [6, 12, 64])
+def test_split_paths_rows_of_different_magnitude(tq2, m):
+    """Row i of x scaled by 10^-(i % 5): four decades between rows."""
+    c = G.random_case(8900 + m, m, 200, 640, residual=False)
+    f = (10.0 ** -(np.arange(m) % 5)).astype(np.float32)[:, None]
+    c["x"] = (c["x"] * f).astype(np.float32)
+    c["name"] = "rows_magnitudes_m%d" % m
+    if m <= 16:
+        assert_case(tq2, c)
+    assert_case(tq2, c, precise=True)
+
+
+def test_split_tile_exponent_across_chunks(tq2):
+    """tq2_gemm_precise at M = 64, K = 1536 (six 256-wide chunks): half the
+    rows start with two all-zero chunks and are 1e-5 after them; the other
+    rows grow tenfold per chunk, so the running exponent of a row falls from
+    chunk to chunk and its sums are rescaled each time."""
+    c = G.random_case(9100, 64, 130, 1536, residual=True)
+    x = c["x"].copy()
+    x[0::2, :512] = 0.0
+    x[0::2, 512:] *= np.float32(1e-5)
+    grow = (10.0 ** np.repeat(np.arange(6) - 3, 256)).astype(np.float32)
+    x[1::2] *= grow[None, :]
+    c["x"] = x
+    c["name"] = "tile_exponent_across_chunks"
+    assert_case(tq2, c, precise=True)
+
+
+@pytest.mark.parametrize("m", [3, 8, 11, 16])
+def test_skinny_passes_with_different_scales(tq2, m):
+    """K = 8320: two full 4096-wide passes and a partial one, x 1e-3 in the
+    first pass and 10 in the rest, so each pass takes its own power of two and
+    the accumulators are rescaled between passes."""
+    c = G.random_case(9000 + m, m, 150, 8320, residual=True)
+    x = c["x"].copy()
+    x[:, :4096] *= np.float32(1e-3)
+    x[:, 4096:] *= np.float32(10.0)
+    c["x"] = x
+    c["name"] = "skinny_pass_scales_m%d" % m
+    assert_case(tq2, c)
+
+
 def test_empty_shapes_are_noops(tq2):
     soa = upload_weight(tq2, G.random_case(1, 1, 8, 128)["aos"], 8, 128)
     x = torch.zeros((0, 128), device="cuda")
