@@ -77,26 +77,29 @@ def measured_traffic(key, source):
 
 
 def run_environment(torch):
-    """Device, HIP runtime and ROCm version, and the GFX clock limits that
-    amd-smi reports (None where the tool is not available)."""
+    """Device, HIP runtime and ROCm version, and the GFX clock levels the
+    driver lists (None where a file is not readable).  Files only: no other
+    program is started from this process."""
+    import glob
     import re
-    import subprocess
-    env = {"device": torch.cuda.get_device_name(0), "hip_runtime": torch.version.hip,
+    props = torch.cuda.get_device_properties(0)
+    env = {"device": torch.cuda.get_device_name(0) or None,
+           "arch": getattr(props, "gcnArchName", None), "hip_runtime": torch.version.hip,
            "rocm": None, "gfx_clock_mhz_max": None, "gfx_clock_mhz_min": None}
     try:
-        txt = subprocess.run(["amd-smi", "version"], capture_output=True, text=True,
-                             timeout=20).stdout
-        m = re.search(r"ROCm version:\s*([0-9.]+)", txt)
-        env["rocm"] = m.group(1) if m else None
-        txt = subprocess.run(["amd-smi", "metric", "-c", "-g", "0"], capture_output=True,
-                             text=True, timeout=20).stdout
-        blk = txt.split("GFX_0:", 1)[1] if "GFX_0:" in txt else ""
-        mx = re.search(r"MAX_CLK:\s*([0-9]+)", blk)
-        mn = re.search(r"MIN_CLK:\s*([0-9]+)", blk)
-        env["gfx_clock_mhz_max"] = int(mx.group(1)) if mx else None
-        env["gfx_clock_mhz_min"] = int(mn.group(1)) if mn else None
-    except (OSError, subprocess.SubprocessError, IndexError):
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip() or None
+    except OSError:
         pass
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                mhz = [int(v) for v in re.findall(r"(\d+)\s*Mhz", f.read(), re.I)]
+        except OSError:
+            continue
+        if mhz:
+            env["gfx_clock_mhz_max"], env["gfx_clock_mhz_min"] = max(mhz), min(mhz)
+            break
     return env
 
 
