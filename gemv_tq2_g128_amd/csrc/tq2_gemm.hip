@@ -1357,12 +1357,19 @@ hipError_t dispatch(int path, const uint8_t* soa, const uint8_t* up, const float
     if (m <= 16) return dispatch_skinny<SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
     return launch_tile<64, 16, 4, 2, 2, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
   }
-  if (m <= 32)
-    return launch_tile<32, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-  if (m <= 64)
-    return launch_tile<64, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-  if (m <= 128)
-    return launch_tile<128, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+  if (m <= 128) {
+    // One row block of the smallest 16-row multiple that covers M: rows past
+    // M still cost x loads and MFMAs (M = 100: 112 rows, 9% faster than 128).
+    switch ((m + 15) / 16) {
+      case 2: return launch_tile<32, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+      case 3: return launch_tile<48, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+      case 4: return launch_tile<64, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+      case 5: return launch_tile<80, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+      case 6: return launch_tile<96, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+      case 7: return launch_tile<112, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+      default: return launch_tile<128, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+    }
+  }
   if (k <= int64_t(kPpMaxKB) * kBlockWeights)
     return launch_pp<96, 48, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
   return launch_tile<96, 48, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);

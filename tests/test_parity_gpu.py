@@ -477,6 +477,19 @@ def test_swiglu_gemm_shapes(tq2, m, n, k):
     assert_swiglu(tq2, G.swiglu_case(5000 + m + n + k, m, n, k))
 
 
+# Path 2 at 16 < M <= 128 runs one row block of the smallest 16-row multiple
+# covering M (32 ... 128 rows): every tile height, at and just past its edge.
+@pytest.mark.parametrize("m", [40, 48, 49, 70, 80, 81, 90, 96, 105, 112, 113])
+def test_tile_heights(tq2, m):
+    c = G.random_case(9200 + m, m, 150, 640, residual=(m % 2 == 0))
+    assert_case(tq2, c)
+
+
+@pytest.mark.parametrize("m", [49, 81, 105])
+def test_swiglu_tile_heights(tq2, m):
+    assert_swiglu(tq2, G.swiglu_case(9300 + m, m, 70, 384))
+
+
 def test_swiglu_same_weight_and_zero_gate(tq2):
     c = G.swiglu_case(6001, 40, 72, 512)
     got, _ = assert_swiglu(tq2, dict(c, same=True, name="same_weight"))
