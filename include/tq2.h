@@ -133,7 +133,10 @@ int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream);
  *      as exact binary16 code * d (oxibonsai-kernels 0.1.5, pipelines.rs,
  *      fields `gemm_tq2_g128_v9_simdgroup` / `gemm_tq2_g128_v10_simdgroup`:
  *      f16-staged operands, f32 accumulation); error within
- *      2e-3 * sum|x w| for |x| <= 65504.
+ *      2e-3 * sum|x w| for |x| <= 65504 whose rows do not average below
+ *      about 1.5e-5 in |x| (under binary16's normal range, 2^-14, the
+ *      rounding of x leaves an absolute error of 2^-25 |w| per element);
+ *      tq2_gemm_precise holds its bound at any magnitude.
  * m == 0 or n == 0 is a no-op.  Errors: INVALID, SHAPE, ALIGN, ALIAS, DEVICE,
  * LAUNCH. */
 int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
