@@ -44,13 +44,13 @@
 // MFMA step s (0..7) takes from every lane the 8 positions 64g + 8s .. +7; the
 // A operand uses the same positions, so each step contracts 32 k's.
 #include "tq2_internal.h"
+#include "tq2_device.h"
 
 namespace tq2 {
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -59,18 +59,6 @@ constexpr int kLdsRow = kChunk + 8;    // binary16 per LDS row (16-byte pad vs b
 constexpr int kPpMaxKB = 96;           // scale blocks per row the ping-pong kernel keeps in LDS (K <= 12288)
 
 __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-
-// Four binary16 pairs (8 weights) of one MFMA step from one code word.
-// `word` holds the step's codes in fields r = 0..3 at bits 2r (first weight
-// of pair r) and 2r + 16 (second weight).  (1024 + 4^r c) * 4^-r - (1024 *
-// 4^-r + 1) = c - 1 exactly; times d stays exact (+-d or 0).
-// v_and_or_b32 with the mask in an SGPR and the constant in a VGPR (gfx9 VOP3
-// instructions take no literal operand).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-  return r;
-}
 
 // Four binary16 pairs (8 weights) of one MFMA step from one code word.
 // `word` holds the step's codes in fields r = 0..3 at bits 2r (first weight
@@ -143,23 +131,6 @@ __device__ __forceinline__ void split_limbs(float a, float b, uint32_t& hi, uint
 // exact, and the sums are scaled back by 2^-e).  mx = 0 gives e = 15.
 __device__ __forceinline__ int prescale_exponent(float mx) {
   return 15 - __builtin_amdgcn_frexp_expf(mx);
-}
-
-// Largest value over the wave (v >= 0): DPP moves (quad permutes, the 8- and
-// 16-lane mirrors, the row broadcasts of lanes 15 and 31) leave it in lane 63.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_move(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
-}
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-  v = fmaxf(v, dpp_move<0xB1, 0xF>(v));
-  v = fmaxf(v, dpp_move<0x4E, 0xF>(v));
-  v = fmaxf(v, dpp_move<0x141, 0xF>(v));
-  v = fmaxf(v, dpp_move<0x140, 0xF>(v));
-  v = fmaxf(v, dpp_move<0x142, 0xA>(v));
-  v = fmaxf(v, dpp_move<0x143, 0xC>(v));
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Store an MT x NO f32 result tile, staged row-major in LDS with row pitch

@@ -33,21 +33,13 @@
 // the binary16 sign positions and OR-ed with 1.0, giving the exact pair
 // ((-1)^b, (-1)^b'), and the 16-term sum is scaled by -d.
 #include "tq2_internal.h"
+#include "tq2_device.h"
 
 namespace tq2 {
 namespace {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
 constexpr int kThreads = 256;
 constexpr uint32_t kMagic = 0x64006400u;   // binary16 pair (1024, 1024)
-
-// v_and_or_b32 with the mask in an SGPR (gfx9 VOP3 takes no literal).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
-  return r;
-}
 
 // The 8 exact binary16 pairs (c_k - 1, c_{k+1} - 1) of one code word.
 __device__ __forceinline__ void decode_word(uint32_t w, uint32_t magic, half2_t (&v)[8]) {
@@ -70,12 +62,6 @@ __device__ __forceinline__ void decode_word(uint32_t w, uint32_t magic, half2_t 
 // most 64) with DPP lane moves: xor 1 and 2 (quad permutes), then the 8- and
 // 16-lane mirrors, then the row broadcasts of lanes 15 and 31.  Afterwards
 // lane G - 1 of each group holds the group's sum.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_move(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xF, false));
-}
-
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (G >= 2) v += dpp_move<0xB1, 0xF>(v);     // quad_perm [1, 0, 3, 2]
