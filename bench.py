@@ -54,15 +54,28 @@ def parse():
     return p.parse_args()
 
 
+KERNEL_HEADERS = ("gemv_tq2_g128_amd/csrc/tq2_internal.h", "gemv_tq2_g128_amd/csrc/tq2_device.h")
+
+
+def kernel_source_digest(source):
+    """sha256 of a kernel source followed by the headers it includes."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for path in (source,) + KERNEL_HEADERS:
+        with open(os.path.join(here, path), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(key, source):
     """HBM bytes per launch of one kernel from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE scaled against a device copy of known size), or
-    None when the kernel source has changed since the counters were taken."""
-    import hashlib
+    None when the kernel source or its headers have changed since the
+    counters were taken."""
     here = os.path.dirname(os.path.abspath(__file__))
     try:
-        with open(os.path.join(here, source), "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        digest = kernel_source_digest(source)
         with open(os.path.join(here, "profiles", "gemv_k4096_n4096_traffic.md")) as f:
             lines = f.read().splitlines()
     except OSError:
