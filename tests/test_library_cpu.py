@@ -103,6 +103,24 @@ def test_argument_checks_before_any_device_work():
     assert r(0, 0, 0, 128) == tq2.TQ2_OK
 
 
+def test_size_limits_before_any_device_work():
+    """Dimensions above 2^30, and on the matrix-core paths K above 2^21 or
+    N * K / 4 code bytes at 2^31 or more, are rejected before any device
+    work (the buffers are far apart, so no alias check fires first)."""
+    g, pg, v = tq2.gemm_ptr, tq2.gemm_precise_ptr, tq2.gemv_ptr
+    X, O = A + (1 << 40), A + (2 << 40)
+    big_k = (1 << 21) + 128
+    assert g(A, X, 0, O, 2, 16, big_k) == tq2.TQ2_ERR_INVALID          # path 1
+    assert g(A, X, 0, O, 40, 16, big_k) == tq2.TQ2_ERR_INVALID         # path 2
+    assert pg(A, X, 0, O, 40, 16, big_k) == tq2.TQ2_ERR_INVALID
+    assert g(A, X, 0, O, 2, 1 << 21, 4096) == tq2.TQ2_ERR_INVALID      # 2^31 code bytes
+    assert g(A, X, 0, O, 40, 1 << 21, 4096) == tq2.TQ2_ERR_INVALID
+    assert g(A, X, 0, O, (1 << 30) + 1, 8, 128) == tq2.TQ2_ERR_INVALID
+    assert g(A, X, 0, O, 4, (1 << 30) + 1, 128) == tq2.TQ2_ERR_INVALID
+    assert v(A, X, 0, O, (1 << 30) + 1, 128) == tq2.TQ2_ERR_INVALID
+    assert v(A, X, 0, O, 8, (1 << 30) + 128) == tq2.TQ2_ERR_INVALID
+
+
 def test_batched_gemv_checks_before_any_device_work():
     b = tq2.gemv_batched_ptr
     X, O = A + 0x100000, A + 0x200000

@@ -310,6 +310,17 @@ def test_skinny_passes_with_different_scales(tq2, m):
     assert_case(tq2, c)
 
 
+@pytest.mark.parametrize("m", [1, 2, 17])
+def test_largest_k(tq2, m):
+    """K = 2^21, the largest K the matrix-core kernels take (their 32-bit
+    buffer offsets span up to 128 x rows of K f32): the GEMV, the skinny
+    kernel (512 passes over K) and the tile kernels, plus the precise one."""
+    c = G.random_case(9400 + m, m, 20, 1 << 21, residual=True)
+    assert_case(tq2, c)
+    if m > 1:
+        assert_case(tq2, c, precise=True)
+
+
 def test_empty_shapes_are_noops(tq2):
     soa = upload_weight(tq2, G.random_case(1, 1, 8, 128)["aos"], 8, 128)
     x = torch.zeros((0, 128), device="cuda")
