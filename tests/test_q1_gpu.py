@@ -115,6 +115,29 @@ def test_q1_decode_workload(tq2):
     assert_q1(tq2, dict(G.q1_decode(True), gemv=True), inplace=True)
 
 
+# Path 1 (M <= 16) scales x by a power of two per wave and K pass before the
+# hi/lo split (the same skinny kernel as TQ2), so 1e-5 holds at any magnitude.
+@pytest.mark.parametrize("m", [3, 8, 13])
+@pytest.mark.parametrize("scale", [1e-6, 3e4])
+def test_q1_split_path_x_magnitudes(tq2, m, scale):
+    c = G.random_case_q1(9500 + m, m, 200, 1280, residual=True)
+    c["x"] = (c["x"] * np.float32(scale)).astype(np.float32)
+    c["residual"] = (c["residual"] * np.float32(scale)).astype(np.float32)
+    c["name"] = "q1_x_scale_%g_m%d" % (scale, m)
+    assert_q1(tq2, c)
+
+
+def test_q1_split_path_passes_with_different_scales(tq2):
+    """K = 8320: x 1e-3 in the first 4096-wide pass and 10 after it."""
+    c = G.random_case_q1(9600, 8, 150, 8320, residual=True)
+    x = c["x"].copy()
+    x[:, :4096] *= np.float32(1e-3)
+    x[:, 4096:] *= np.float32(10.0)
+    c["x"] = x
+    c["name"] = "q1_pass_scales_m8"
+    assert_q1(tq2, c)
+
+
 Q1_GEMM_SHAPES = [(2, 17, 128), (9, 100, 384), (16, 257, 1024), (5, 4100, 4224), (12, 8200, 2176),
                   (17, 200, 384), (33, 100, 256),
                   (64, 129, 384), (100, 300, 1024), (128, 64, 256), (129, 191, 384),
