@@ -150,6 +150,36 @@ def capture(torch, stream, fn, count):
     return g
 
 
+def exact_graphs(torch, stream, fn, calls, chunk=2048):
+    """HIP graphs that together make exactly `calls` calls fn(0), fn(1), ...:
+    one graph of `chunk` calls replayed as often as it fits, and one graph
+    for the remainder.  Returns [(graph, replays)]."""
+    full, rest = divmod(calls, chunk)
+    out = []
+    if full:
+        out.append((capture(torch, stream, fn, chunk), full))
+    if rest:
+        out.append((capture(torch, stream, lambda i: fn(full * chunk + i), rest), 1))
+    return out
+
+
+def time_graphs(torch, graphs, stream):
+    """Replay [(graph, replays)] back to back between two events on the stream
+    the kernels run on; returns (event ms, wall s)."""
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for graph, replays in graphs:
+            for _ in range(replays):
+                graph.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), time.perf_counter() - t0
+
+
 def cpu_baseline(case, seconds):
     """The oracle as it stands, on the host, single BLAS thread."""
     from threadpoolctl import threadpool_limits
@@ -471,11 +501,16 @@ def main():
         if st != 0:
             raise RuntimeError("tq2_gemv failed: %s" % tq2.status_string(st))
 
-    graph = capture(torch, stream, gemv_call, pool)
-    time_graph(torch, graph, max(1, args.warmup // pool), stream)
-    replays = max(1, int(math.ceil(args.steps / pool)))
-    steps = replays * pool
-    ms, wall = time_graph(torch, graph, replays, stream)
+    # Exactly `warmup` untimed calls, then exactly `steps` timed ones; call i
+    # reads weight copy i % pool, so consecutive calls read different copies.
+    steps, warmup = max(1, args.steps), max(0, args.warmup)
+    if warmup:
+        warm = exact_graphs(torch, stream, gemv_call, warmup)
+        time_graphs(torch, warm, stream)
+        del warm
+    timed = exact_graphs(torch, stream, gemv_call, steps)
+    ms, wall = time_graphs(torch, timed, stream)
+    del timed
     us_per_call = ms * 1e3 / steps
     gbs = nbytes / (us_per_call * 1e-6) / 1e9
 
@@ -485,7 +520,7 @@ def main():
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": max(1, args.warmup // pool) * pool,
+        "warmup": warmup,
         "ms_per_step": round(ms / steps, 6),
         "higher_is_better": True,
         "scaling": "weak",
