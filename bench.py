@@ -318,6 +318,40 @@ def swiglu_bench(torch, tq2, G, dev, stream, args):
     }
 
 
+def launch_floor(torch, dev, stream, base, pool, sb, blocks, steps):
+    """Reference launches with the decode GEMV's grid (`blocks` blocks of 256
+    threads) from libtq2_probe.so: an empty kernel, and a plain streaming read
+    of one weight copy's sb bytes (copies rotated as for the GEMV).  Returns
+    None when the probe library is not built."""
+    import ctypes
+    from gemv_tq2_g128_amd import build as B
+    path = os.path.join(B.PKG_DIR, B.PROBE_LIB_NAME)
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    lib.tq2_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_void_p]
+    lib.tq2_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    sink = torch.zeros(blocks, dtype=torch.int32, device=dev)
+
+    def empty_call(i):
+        if lib.tq2_probe_empty(blocks, torch.cuda.current_stream(dev).cuda_stream) != 0:
+            raise RuntimeError("tq2_probe_empty failed")
+
+    def read_call(i):
+        if lib.tq2_probe_read(base + (i % pool) * sb, sb, sink.data_ptr(), blocks,
+                              torch.cuda.current_stream(dev).cuda_stream) != 0:
+            raise RuntimeError("tq2_probe_read failed")
+
+    out = {"grid": "%d blocks x 256 threads" % blocks, "read_bytes": sb, "calls": steps}
+    for name, fn in (("empty", empty_call), ("read", read_call)):
+        time_graphs(torch, exact_graphs(torch, stream, fn, min(steps, 512)), stream)
+        ms, _ = time_graphs(torch, exact_graphs(torch, stream, fn, steps), stream)
+        out[name + "_us_per_launch"] = round(ms * 1e3 / steps, 3)
+    out["read_gbs"] = round(sb / (out["read_us_per_launch"] * 1e-6) / 1e9, 2)
+    return out
+
+
 def gemv_sweep(torch, tq2, G, dev, stream, args):
     """Decode GEMV with residual at N = K = 4096, 8192 and 16384 (config 2's
     code and scale distributions, seed 20 + N/4096), each weight rotated over
@@ -540,6 +574,13 @@ def main():
                      "traffic_unit": "bytes per launch", "kernel": "gemv_kernel",
                      "us_per_launch": round(us_per_call, 3)},
     }
+
+    # ---- what one launch of the GEMV's grid costs, and a plain read of the
+    # same bytes in one such launch (reference kernels, not the library) -------
+    floor = launch_floor(torch, dev, stream, base, pool, sb, (n + 7) // 8, steps)
+    if floor is not None:
+        floor["gemv_us_per_launch"] = round(us_per_call, 3)
+        result["launch_floor_k4096_n4096"] = floor
 
     # ---- batched decode GEMV: 16 K = N = 4096 weights per call ----------------
     if not args.no_batched:

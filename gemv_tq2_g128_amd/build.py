@@ -33,12 +33,22 @@ def hipcc_path():
     return p if os.path.exists(p) else "hipcc"
 
 
+PROBE_LIB_NAME = "libtq2_probe.so"
+PROBE_SOURCES = ["tq2_probe.hip"]
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into ``libtq2.so``; returns the library path."""
-    out = os.path.join(PKG_DIR, LIB_NAME)
+    """Compile every HIP source into ``libtq2.so`` (and the benchmark's
+    reference kernels into ``libtq2_probe.so``); returns the library path."""
+    _compile(PROBE_SOURCES, PROBE_LIB_NAME, verbose)
+    return _compile(SOURCES, LIB_NAME, verbose)
+
+
+def _compile(sources, lib_name, verbose):
+    out = os.path.join(PKG_DIR, lib_name)
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc_path(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -121,6 +121,24 @@ def test_size_limits_before_any_device_work():
     assert v(A, X, 0, O, 8, (1 << 30) + 128) == tq2.TQ2_ERR_INVALID
 
 
+def test_probe_library_for_the_benchmark():
+    """libtq2_probe.so (reference launches for bench.py, built beside libtq2)
+    exports its two entry points and rejects bad arguments before any launch."""
+    import ctypes
+    from gemv_tq2_g128_amd import build as B
+    path = os.path.join(B.PKG_DIR, B.PROBE_LIB_NAME)
+    assert os.path.exists(path), "run the build first"
+    lib = ctypes.CDLL(path, mode=ctypes.RTLD_LOCAL)
+    lib.tq2_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_void_p]
+    lib.tq2_probe_empty.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    assert lib.tq2_probe_read(None, 4096, A, 8, None) == -1
+    assert lib.tq2_probe_read(A, 4096, None, 8, None) == -1
+    assert lib.tq2_probe_read(A, 4100, A + 0x100000, 8, None) == -1
+    assert lib.tq2_probe_read(A, 4096, A + 0x100000, 0, None) == -1
+    assert lib.tq2_probe_empty(0, None) == -1
+
+
 def test_batched_gemv_checks_before_any_device_work():
     b = tq2.gemv_batched_ptr
     X, O = A + 0x100000, A + 0x200000
