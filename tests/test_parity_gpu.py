@@ -411,6 +411,13 @@ def test_gemv_batched_matches_oracle_at_decode_size(tq2):
     _batched_check(tq2, specs, "decode")
 
 
+def test_gemv_batched_ragged(tq2):
+    """Rows off the block size, K = 1152 (72 words per row: two 128-lane row
+    slots per block, masked lanes), with and without residual, some in place."""
+    specs = [(3700 + 13 * i, 1152, i % 3 != 2, None, i % 3 == 0) for i in range(9)]
+    _batched_check(tq2, specs, "ragged")
+
+
 # ---------------------------------------------------------------------------
 # tq2_gemm_precise: f32-class accuracy (1e-5 * S) at every M.
 # ---------------------------------------------------------------------------
