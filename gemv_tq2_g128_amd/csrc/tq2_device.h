@@ -8,6 +8,17 @@ namespace tq2 {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over `bytes` bytes at `base`: a load whose per-lane
+// offset (plus the instruction offset) reaches past the end returns zeros.
+// The hardware range check does not include the scalar offset operand, so a
+// variable offset that must be range-checked goes into the per-lane offset.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
+                                           0x00020000);
+}
+
 // v_and_or_b32 with the mask in an SGPR (gfx9 VOP3 takes no literal).
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
   uint32_t r;

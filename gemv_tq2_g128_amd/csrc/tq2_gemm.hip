@@ -176,19 +176,11 @@ __device__ __forceinline__ void store_tile(const float* tile, int tid, int m0, i
   }
 }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Raw buffer resource over `bytes` bytes at `base`: a load whose per-lane
-// offset (plus the instruction offset) reaches past the end returns zeros.
-// The hardware range check does not include the scalar offset operand, so
-// every variable offset here goes into the per-lane offset and the scalar
-// offset stays 0.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
-                                           0x00020000);
-}
+// Buffer loads (make_rsrc) keep every variable offset in the per-lane
+// offset and the scalar offset 0, so ragged tails read zeros.
 
 // Block tile MT x (WN*NW); WN waves split the columns, WK waves split each
 // 256-wide chunk's eight MFMA steps (their partial sums meet in LDS at the

@@ -13,8 +13,11 @@
 // registers for all ROWS rows.
 //
 // Latency.  The code words and scales of all ROWS rows are loaded with
-// clamped, branch-free addresses before any arithmetic, so one block keeps
-// ROWS loads per lane in flight instead of paying the HBM latency per row.
+// branch-free buffer loads before any arithmetic, so one block keeps ROWS
+// loads per lane in flight instead of paying the HBM latency per row.  When
+// a block is one row slot its rows are block-uniform: each row's offset is a
+// scalar operand and the lane's offset is shared by all rows, so the loads
+// cost no per-row vector address arithmetic.
 // The lane's x values are loaded before them: loads complete in issue order,
 // so row r's arithmetic starts as soon as row r's weights have arrived.
 //
@@ -79,20 +82,15 @@ __device__ __forceinline__ float group_sum(float v) {
 template <Fmt F>
 __device__ __forceinline__ int words_per_row(int k) { return F == Fmt::kQ1 ? k >> 5 : k >> 4; }
 
-template <Fmt F>
-__device__ __forceinline__ uint32_t unit_word(const uint32_t* crow, unsigned u) {
-  if constexpr (F == Fmt::kQ1) return crow[u >> 1] >> (8 * (u & 1));
-  return crow[u];
-}
 
 __device__ __forceinline__ float dot16(const half2_t (&v)[8], const float (&xv)[16]) {
-  float s0 = 0.f, s1 = 0.f;
+  float s = 0.f;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    s0 = __builtin_fmaf(xv[2 * p], float(v[p][0]), s0);
-    s1 = __builtin_fmaf(xv[2 * p + 1], float(v[p][1]), s1);
+    s = __builtin_fmaf(xv[2 * p], float(v[p][0]), s);
+    s = __builtin_fmaf(xv[2 * p + 1], float(v[p][1]), s);
   }
-  return s0 + s1;
+  return s;
 }
 
 // Sum of x[t] * (2 b_t - 1) over the 16 weights of one Q1 unit (exact +-1
@@ -122,28 +120,69 @@ __device__ __forceinline__ void load_x16(const float* __restrict__ x, int wc, fl
   }
 }
 
+// The code word holding lane unit u of a row whose words start at byte
+// `row_off` (scalar) + `lane_row_off` (per lane) of the resource.
+template <Fmt F>
+__device__ __forceinline__ uint32_t unit_word_at(rsrc_t rc, uint32_t lane_row_off,
+                                                 uint32_t row_off, unsigned u) {
+  if constexpr (F == Fmt::kQ1)
+    return __builtin_amdgcn_raw_buffer_load_b32(rc, lane_row_off + (u >> 1) * 4u, row_off, 0) >>
+           (8 * (u & 1));
+  return __builtin_amdgcn_raw_buffer_load_b32(rc, lane_row_off + u * 4u, row_off, 0);
+}
+
+// Row `r` of a block whose first row is blk_row0, as an index into the
+// block's resources: with one slot per block (SLOTS == 1) r is block-uniform
+// and clamped to the last row, so every access stays inside the resource;
+// otherwise r is per lane and rows past the end read zeros through the range
+// check (their sums are never stored).
+template <int SLOTS>
+__device__ __forceinline__ uint32_t block_row(int blk_row0, int r, int n_rows) {
+  if constexpr (SLOTS == 1) return uint32_t(min(blk_row0 + r, n_rows - 1) - blk_row0);
+  return uint32_t(r);
+}
+
+// Code word and scale of lane unit u of block row `row`.  SLOTS == 1: the
+// row's offset is a scalar (the scalar offset operand) and the lane's offset
+// is the same for every row, so a row costs no vector address arithmetic.
+template <int SLOTS, Fmt F>
+__device__ __forceinline__ void load_row(rsrc_t rc, rsrc_t rs, uint32_t row, uint32_t wrow,
+                                         uint32_t kb_count, unsigned u, uint32_t& cw,
+                                         uint32_t& db) {
+  if constexpr (SLOTS == 1) {
+    cw = unit_word_at<F>(rc, 0u, row * wrow * 4u, u);
+    db = __builtin_amdgcn_raw_buffer_load_b16(rs, (u >> 3) * 2u, row * kb_count * 2u, 0);
+  } else {
+    cw = unit_word_at<F>(rc, row * wrow * 4u, 0u, u);
+    db = __builtin_amdgcn_raw_buffer_load_b16(rs, (row * kb_count + (u >> 3)) * 2u, 0, 0);
+  }
+}
+
 // Load the 16 x values of lane unit wc (16 weights), then ROWS code words
 // and scales of it.  Vector loads return in issue order, so the x loads (L2
 // hits) go first: the arithmetic of row 0 then waits only for row 0's
 // weights, and each later row's arithmetic overlaps the arrival of the rest.
-template <int ROWS, Fmt F>
+// The buffer resources start at the block's first row `blk_row0` and cover
+// its rows that exist.
+template <int ROWS, int SLOTS, Fmt F>
 __device__ __forceinline__ void load_segment(const uint32_t* __restrict__ codes,
                                              const uint16_t* __restrict__ scales,
-                                             const float* __restrict__ x, int row0, int n_rows,
-                                             int k, int kb_count, int wc, uint32_t (&cw)[ROWS],
-                                             uint32_t (&db)[ROWS], float (&xv)[16]) {
-  const unsigned uwc = unsigned(wc);            // lane offset: 32-bit, base pointer uniform
-  const int wrow = words_per_row<F>(k);
+                                             const float* __restrict__ x, int blk_row0,
+                                             int slot, int n_rows, int k, int kb_count, int wc,
+                                             uint32_t (&cw)[ROWS], uint32_t (&db)[ROWS],
+                                             float (&xv)[16]) {
+  const unsigned uwc = unsigned(wc);
+  const uint32_t wrow = uint32_t(words_per_row<F>(k));
+  const uint32_t live_rows = uint32_t(min(SLOTS * ROWS, n_rows - blk_row0));
+  const rsrc_t rc = make_rsrc(codes + size_t(blk_row0) * wrow, live_rows * wrow * 4u);
+  const rsrc_t rs = make_rsrc(scales + size_t(blk_row0) * uint32_t(kb_count),
+                              live_rows * uint32_t(kb_count) * 2u);
   load_x16(x, wc, xv);
   __builtin_amdgcn_sched_barrier(0);            // keep the x loads first
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    const int row = min(row0 + r, n_rows - 1);
-    const uint32_t* crow = codes + size_t(row) * wrow;
-    const uint16_t* srow = scales + size_t(row) * kb_count;
-    cw[r] = unit_word<F>(crow, uwc);
-    db[r] = srow[uwc >> 3];
-  }
+  for (int r = 0; r < ROWS; ++r)
+    load_row<SLOTS, F>(rc, rs, block_row<SLOTS>(blk_row0, slot * ROWS + r, n_rows), wrow,
+                       uint32_t(kb_count), uwc, cw[r], db[r]);
 }
 
 template <int ROWS, Fmt F>
@@ -186,7 +225,6 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
   const int lw = SLOTS == 1 ? t : t % LPS;      // word index inside a K segment
   const int wpr = k >> 4;                       // lane units (16 weights) per row
   const int kb_count = k >> 7;
-  const int row0 = blk * OUTS + slot * ROWS;
   // The output row this thread finishes (if it is its group's last lane),
   // and its residual, loaded first so that its latency is hidden.
   const int g = t % G;
@@ -204,20 +242,21 @@ __device__ __forceinline__ void gemv_block(const uint32_t* __restrict__ codes,
   float xv[16];
   if constexpr (ONE_SEG) {
     if (wpr == LPS) {                           // every lane has a unit: no masking
-      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, k, kb_count, lw, cw, db, xv);
+      load_segment<ROWS, SLOTS, F>(codes, scales, x, blk * OUTS, slot, n_rows, k, kb_count, lw,
+                                   cw, db, xv);
       accumulate_segment<ROWS, F>(cw, db, xv, true, part);
     } else {
       const bool live = lw < wpr;
-      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, k, kb_count, live ? lw : wpr - 1,
-                            cw, db, xv);
+      load_segment<ROWS, SLOTS, F>(codes, scales, x, blk * OUTS, slot, n_rows, k, kb_count,
+                                   live ? lw : wpr - 1, cw, db, xv);
       accumulate_segment<ROWS, F>(cw, db, xv, live, part);
     }
   } else {
     for (int seg = 0; seg < wpr; seg += LPS) {
       const int w = seg + lw;
       const bool live = w < wpr;
-      load_segment<ROWS, F>(codes, scales, x, row0, n_rows, k, kb_count, live ? w : wpr - 1,
-                            cw, db, xv);
+      load_segment<ROWS, SLOTS, F>(codes, scales, x, blk * OUTS, slot, n_rows, k, kb_count,
+                                   live ? w : wpr - 1, cw, db, xv);
       accumulate_segment<ROWS, F>(cw, db, xv, live, part);
     }
   }
@@ -300,7 +339,6 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   const int wpr = k >> 4;                       // lane units (16 weights) per row
   const int wrow = words_per_row<F>(k);
   const int kb_count = k >> 7;
-  const int out0 = blockIdx.x * OUTS + slot * HALF;
 
   float part[ROWS];
 #pragma unroll
@@ -309,18 +347,21 @@ __global__ __launch_bounds__(kThreads) void gemv_swiglu_kernel(
   uint32_t db[ROWS];
   float xv[16];
   // Rows 0..HALF-1 from the gate weight, HALF..ROWS-1 from the up weight.
+  const int blk_row0 = blockIdx.x * OUTS;
+  const uint32_t live_rows = uint32_t(min(OUTS, n_rows - blk_row0));
+  const uint32_t uwrow = uint32_t(wrow), ukb = uint32_t(kb_count);
+  const rsrc_t rc[2] = {make_rsrc(gcodes + size_t(blk_row0) * uwrow, live_rows * uwrow * 4u),
+                        make_rsrc(ucodes + size_t(blk_row0) * uwrow, live_rows * uwrow * 4u)};
+  const rsrc_t rs[2] = {make_rsrc(gscales + size_t(blk_row0) * ukb, live_rows * ukb * 2u),
+                        make_rsrc(uscales + size_t(blk_row0) * ukb, live_rows * ukb * 2u)};
   auto load = [&](int wc) {
-    const unsigned uwc = unsigned(wc);
     load_x16(x, wc, xv);                        // x first, as in load_segment
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const int row = min(out0 + (r % HALF), n_rows - 1);
-      const uint32_t* crow = (r < HALF ? gcodes : ucodes) + size_t(row) * wrow;
-      const uint16_t* srow = (r < HALF ? gscales : uscales) + size_t(row) * kb_count;
-      cw[r] = unit_word<F>(crow, uwc);
-      db[r] = srow[uwc >> 3];
-    }
+    for (int r = 0; r < ROWS; ++r)
+      load_row<SLOTS, F>(rc[r / HALF], rs[r / HALF],
+                         block_row<SLOTS>(blk_row0, slot * HALF + r % HALF, n_rows), uwrow, ukb,
+                         unsigned(wc), cw[r], db[r]);
   };
   if constexpr (ONE_SEG) {
     const bool live = lw < wpr;
