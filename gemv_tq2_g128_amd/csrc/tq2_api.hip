@@ -208,8 +208,17 @@ int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream) 
         return TQ2_ERR_ALIAS;
     }
   }
+  // Each k's launch is one grid of at most ceil(n / 4) row blocks per problem;
+  // a grid that would not fit is rejected before anything is enqueued.
   bool any = false;
-  for (int i = 0; i < count; ++i) any = any || problems[i].n > 0;
+  for (int i = 0; i < count; ++i) {
+    if (problems[i].n == 0) continue;
+    any = true;
+    int64_t blocks = 0;
+    for (int j = 0; j < count; ++j)
+      if (problems[j].n > 0 && problems[j].k == problems[i].k) blocks += (problems[j].n + 3) / 4;
+    if (blocks > INT32_MAX) return TQ2_ERR_INVALID;
+  }
   if (!any) return TQ2_OK;
   const int dst = check_device();
   if (dst != TQ2_OK) return dst;

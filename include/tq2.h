@@ -114,8 +114,9 @@ typedef struct tq2_gemv_problem {
  * problems with n == 0 are no-ops.  Every problem is checked before anything
  * is enqueued; a failed launch (TQ2_ERR_LAUNCH) may leave the launches for
  * smaller k already enqueued.  Errors: INVALID (null problems with count > 0,
- * count < 0 or count > TQ2_GEMV_BATCH_MAX, or a problem's argument), SHAPE,
- * ALIGN, ALIAS, DEVICE, LAUNCH. */
+ * count < 0 or count > TQ2_GEMV_BATCH_MAX, a problem's argument, or the
+ * problems of one k with a sum of ceil(n / 4) above 2^31 - 1: their grid),
+ * SHAPE, ALIGN, ALIAS, DEVICE, LAUNCH. */
 int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream);
 
 /* Batched matmul for any M >= 1: out[m, n] = residual[m, n] + sum_k x[m, k] w[n, k].

@@ -158,6 +158,13 @@ def test_batched_gemv_checks_before_any_device_work():
     assert b([(A, X, O + 0x100, O, 8, 128), (A, X, 0, O + 0x100, 8, 128)]) == tq2.TQ2_ERR_ALIAS
     # empty problems are skipped; an all-empty batch is a no-op
     assert b([(0, 0, 0, 0, 0, 128), (0, 0, 0, 0, 0, 256)]) == tq2.TQ2_OK
+    # one k's problems whose grid (ceil(n / 4) row blocks each) would pass
+    # 2^31 - 1 blocks: rejected before anything is enqueued, even after a
+    # smaller k's group that fits (far-apart buffers, so no alias fires)
+    big = [(A + (i << 38), A + (1 << 44) + (i << 38), 0, A + (2 << 44) + (i << 38), 1 << 30, 256)
+           for i in range(8)]
+    small = [(A + (3 << 44), A + (3 << 44) + (1 << 40), 0, A + (3 << 44) + (2 << 40), 8, 128)]
+    assert b(small + big) == tq2.TQ2_ERR_INVALID
 
 
 def test_swiglu_checks_before_any_device_work():
