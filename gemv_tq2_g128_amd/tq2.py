@@ -268,6 +268,28 @@ def _require(t, dtype, numel: int, what: str):
         raise ValueError("%s must have %d elements, got %d" % (what, numel, t.numel()))
 
 
+def _one_device(*named):
+    """The device of the given (name, tensor) pairs, which must all be the
+    same: a kernel reads and writes only memory of the device it runs on."""
+    dev = None
+    for what, t in named:
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other tensors on %s" % (what, t.device, dev))
+    return dev
+
+
+def _launch(dev, fn, *args):
+    """Run a raw call with `dev` as the current device and its current stream:
+    a launch on the null stream goes to the current device."""
+    torch = _torch()
+    with torch.cuda.device(dev):
+        return fn(*args, _stream_handle(dev))
+
+
 def reformat_aos_to_soa(aos, n: int, k: int, out=None, fmt: str = "tq2"):
     """AoS block bytes (uint8 device tensor) -> resident SoA weight (uint8).
     fmt: "tq2" (34-byte TQ2_0_g128 blocks) or "q1" (18-byte Q1_g128 blocks)."""
@@ -280,9 +302,9 @@ def reformat_aos_to_soa(aos, n: int, k: int, out=None, fmt: str = "tq2"):
     if out is None:
         out = torch.empty(soa_b(n, k), dtype=torch.uint8, device=aos.device)
     _require(out, torch.uint8, soa_b(n, k), "soa")
+    dev = _one_device(("aos", aos), ("soa", out))
     call = q1_reformat_aos_to_soa_ptr if fmt == "q1" else reformat_aos_to_soa_ptr
-    _check(call(aos.data_ptr(), out.data_ptr(), n, k, _stream_handle(aos.device)),
-           "reformat_aos_to_soa")
+    _check(_launch(dev, call, aos.data_ptr(), out.data_ptr(), n, k), "reformat_aos_to_soa")
     return out
 
 
@@ -296,9 +318,11 @@ def gemv(soa, x, n: int, k: int, residual=None, out=None, fmt: str = "tq2"):
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=x.device)
     _require(out, torch.float32, n, "out")
+    dev = _one_device(("x", x), ("soa", soa), ("residual", residual), ("out", out))
     call = q1_gemv_ptr if fmt == "q1" else gemv_ptr
-    _check(call(soa.data_ptr(), x.data_ptr(), residual.data_ptr() if residual is not None else 0,
-                out.data_ptr(), n, k, _stream_handle(x.device)), "gemv")
+    _check(_launch(dev, call, soa.data_ptr(), x.data_ptr(),
+                   residual.data_ptr() if residual is not None else 0, out.data_ptr(), n, k),
+           "gemv")
     return out
 
 
@@ -320,9 +344,10 @@ def gemm(soa, x, n: int, k: int, residual=None, out=None, precise: bool = False,
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _require(out, torch.float32, m * n, "out")
+    dev = _one_device(("x", x), ("soa", soa), ("residual", residual), ("out", out))
     call = q1_gemm_ptr if fmt == "q1" else (gemm_precise_ptr if precise else gemm_ptr)
-    _check(call(soa.data_ptr(), x.data_ptr(), residual.data_ptr() if residual is not None else 0,
-                out.data_ptr(), m, n, k, _stream_handle(x.device)),
+    _check(_launch(dev, call, soa.data_ptr(), x.data_ptr(),
+                   residual.data_ptr() if residual is not None else 0, out.data_ptr(), m, n, k),
            "gemm_precise" if precise else "gemm")
     return out
 
@@ -345,11 +370,14 @@ def gemv_batched(problems):
         if out is None:
             out = torch.empty(n, dtype=torch.float32, device=p["x"].device)
         _require(out, torch.float32, n, "out")
-        dev = p["x"].device
+        d = _one_device(("x", p["x"]), ("soa", p["soa"]), ("residual", res), ("out", out))
+        if dev is not None and d != dev:
+            raise ValueError("every problem of one batch must be on one device")
+        dev = d
         outs.append(out)
         raw.append((p["soa"].data_ptr(), p["x"].data_ptr(), res.data_ptr() if res is not None else 0,
                     out.data_ptr(), n, k))
-    _check(gemv_batched_ptr(raw, _stream_handle(dev)), "gemv_batched")
+    _check(_launch(dev, gemv_batched_ptr, raw), "gemv_batched")
     return outs
 
 
@@ -366,7 +394,8 @@ def gate_up_swiglu(gate_soa, up_soa, x, n: int, k: int, out=None, fmt: str = "tq
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _require(out, torch.float32, m * n, "out")
+    dev = _one_device(("x", x), ("gate_soa", gate_soa), ("up_soa", up_soa), ("out", out))
     call = q1_gate_up_swiglu_ptr if fmt == "q1" else gate_up_swiglu_ptr
-    _check(call(gate_soa.data_ptr(), up_soa.data_ptr(), x.data_ptr(), out.data_ptr(), m, n, k,
-                _stream_handle(x.device)), "gate_up_swiglu")
+    _check(_launch(dev, call, gate_soa.data_ptr(), up_soa.data_ptr(), x.data_ptr(),
+                   out.data_ptr(), m, n, k), "gate_up_swiglu")
     return out

@@ -234,3 +234,13 @@ def test_device_check_without_gpu():
     st = tq2.gemv_batched_ptr([(A, A + 0x100000, 0, A + 0x200000, 8, 128),
                                (A, A + 0x100000, 0, A + 0x200100, 8, 128)])
     assert st == tq2.TQ2_ERR_DEVICE
+
+
+def test_binding_requires_one_device():
+    """The torch front end refuses tensors on different devices (a kernel only
+    reaches memory of the device it runs on); None entries are skipped."""
+    import torch
+    a, b = torch.empty(1), torch.empty(1, device="meta")
+    assert tq2._one_device(("x", a), ("residual", None), ("out", a)) == a.device
+    with pytest.raises(ValueError, match="out is on meta"):
+        tq2._one_device(("x", a), ("out", b))
