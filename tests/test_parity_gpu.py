@@ -321,6 +321,45 @@ def test_largest_k(tq2, m):
         assert_case(tq2, c, precise=True)
 
 
+def test_largest_weight(tq2):
+    """N = 2^21 - 1 rows at K = 4096: 2^31 - 1024 code bytes, just under the
+    limit the matrix-core kernels take (their buffer offsets are 32-bit).
+    The rows repeat with a prime period of 4099, so an offset that wrapped or
+    lost its high bits would read another row.  Sampled rows (the first, the
+    last, both sides of period boundaries and the middle) are checked against
+    the oracle on every path: GEMV, skinny, 16-column tile, ping-pong, precise."""
+    n, k, period = (1 << 21) - 1, 4096, 4099
+    row_bytes = (k // 128) * 34
+    base = G.make_weight(np.random.default_rng(9500), period, k)
+    aos = np.tile(base, -(-n // period))[: n * row_bytes]
+    print("largest weight: n=%d k=%d, %d AoS bytes" % (n, k, aos.size), flush=True)
+    soa = upload_weight(tq2, aos, n, k)
+    del aos
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, period - 1, period, n // 2, n // 2 + 1, n - period - 1, n - period]
+                    + list(range(n - 64, n)))
+    aos_rows = np.concatenate([base[(r % period) * row_bytes:(r % period + 1) * row_bytes]
+                               for r in rows])
+    rng = np.random.default_rng(9501)
+    for m, precise in ((1, False), (2, False), (40, False), (200, False), (40, True)):
+        x = rng.standard_normal((m, k), dtype=np.float32)
+        print("largest weight: m=%d precise=%s" % (m, precise), flush=True)
+        if m == 1:
+            y = tq2.gemv(soa, _dev(x).reshape(-1), n, k).reshape(1, n)
+            path = 0
+        else:
+            y = tq2.gemm(soa, _dev(x), n, k, precise=precise)
+            path = 1 if precise else tq2.gemm_path(m, n, k)
+        torch.cuda.synchronize()
+        got = y[:, torch.from_numpy(rows).cuda()].cpu().numpy()
+        del y
+        ref = oracle.matmul(aos_rows, x, len(rows), k, None)
+        sc = oracle.error_scale(aos_rows, x, len(rows), k, None)
+        ok, msg = check(got, ref, sc, path, "largest weight m=%d%s" % (m, " precise" * precise))
+        print(msg, flush=True)
+        assert ok, msg
+
+
 def test_empty_shapes_are_noops(tq2):
     soa = upload_weight(tq2, G.random_case(1, 1, 8, 128)["aos"], 8, 128)
     x = torch.zeros((0, 128), device="cuda")
