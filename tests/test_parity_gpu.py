@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import tq2_inputs as G
-from tests.parity import check
+from tests.parity import TOL, check, check_swiglu
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -321,41 +321,63 @@ def test_largest_k(tq2, m):
         assert_case(tq2, c, precise=True)
 
 
-def test_largest_weight(tq2):
-    """N = 2^21 - 1 rows at K = 4096: 2^31 - 1024 code bytes, just under the
-    limit the matrix-core kernels take (their buffer offsets are 32-bit).
-    The rows repeat with a prime period of 4099, so an offset that wrapped or
-    lost its high bits would read another row.  Sampled rows (the first, the
-    last, both sides of period boundaries and the middle) are checked against
-    the oracle on every path: GEMV, skinny, 16-column tile, ping-pong, precise."""
+@pytest.mark.parametrize("fmt", ["tq2", "q1"])
+def test_largest_weight(tq2, fmt):
+    """N = 2^21 - 1 rows at K = 4096: N * K / 4 = 2^31 - 1024, just under the
+    limit the matrix-core kernels take (their buffer offsets are 32-bit; a
+    TQ2 weight then has 2^31 - 1024 code bytes).  The rows repeat with a
+    prime period of 4099, so an offset that wrapped or lost its high bits
+    would read another row.  Sampled rows (the first, the last, both sides of
+    period boundaries and the middle) are checked against the oracle on every
+    path: GEMV, skinny, 16-column tile, ping-pong and precise, and for TQ2 the
+    fused SwiGLU (gate = up) at M = 1 and M = 40."""
     n, k, period = (1 << 21) - 1, 4096, 4099
-    row_bytes = (k // 128) * 34
-    base = G.make_weight(np.random.default_rng(9500), period, k)
+    q1 = fmt == "q1"
+    row_bytes = (k // 128) * (18 if q1 else 34)
+    make = G.make_weight_q1 if q1 else G.make_weight
+    base = make(np.random.default_rng(9500), period, k)
     aos = np.tile(base, -(-n // period))[: n * row_bytes]
-    print("largest weight: n=%d k=%d, %d AoS bytes" % (n, k, aos.size), flush=True)
-    soa = upload_weight(tq2, aos, n, k)
+    print("largest weight %s: n=%d k=%d, %d AoS bytes" % (fmt, n, k, aos.size), flush=True)
+    soa = tq2.reformat_aos_to_soa(_dev(aos), n, k, fmt=fmt)
     del aos
     torch.cuda.synchronize()
     rows = np.array([0, 1, period - 1, period, n // 2, n // 2 + 1, n - period - 1, n - period]
                     + list(range(n - 64, n)))
     aos_rows = np.concatenate([base[(r % period) * row_bytes:(r % period + 1) * row_bytes]
                                for r in rows])
+    idx = torch.from_numpy(rows).cuda()
     rng = np.random.default_rng(9501)
-    for m, precise in ((1, False), (2, False), (40, False), (200, False), (40, True)):
+    cases = ((1, False), (2, False), (40, False), (200, False)) + (() if q1 else ((40, True),))
+    for m, precise in cases:
         x = rng.standard_normal((m, k), dtype=np.float32)
-        print("largest weight: m=%d precise=%s" % (m, precise), flush=True)
+        print("largest weight %s: m=%d precise=%s" % (fmt, m, precise), flush=True)
         if m == 1:
-            y = tq2.gemv(soa, _dev(x).reshape(-1), n, k).reshape(1, n)
+            y = tq2.gemv(soa, _dev(x).reshape(-1), n, k, fmt=fmt).reshape(1, n)
             path = 0
         else:
-            y = tq2.gemm(soa, _dev(x), n, k, precise=precise)
+            y = tq2.gemm(soa, _dev(x), n, k, precise=precise, fmt=fmt)
             path = 1 if precise else tq2.gemm_path(m, n, k)
         torch.cuda.synchronize()
-        got = y[:, torch.from_numpy(rows).cuda()].cpu().numpy()
+        got = y[:, idx].cpu().numpy()
         del y
-        ref = oracle.matmul(aos_rows, x, len(rows), k, None)
-        sc = oracle.error_scale(aos_rows, x, len(rows), k, None)
-        ok, msg = check(got, ref, sc, path, "largest weight m=%d%s" % (m, " precise" * precise))
+        ref = oracle.matmul(aos_rows, x, len(rows), k, None, fmt=fmt)
+        sc = oracle.error_scale(aos_rows, x, len(rows), k, None, fmt=fmt)
+        ok, msg = check(got, ref, sc, path, "largest %s m=%d%s" % (fmt, m, " precise" * precise))
+        print(msg, flush=True)
+        assert ok, msg
+    if q1:
+        return
+    for m in (1, 40):
+        x = rng.standard_normal((m, k), dtype=np.float32)
+        print("largest weight swiglu: m=%d" % m, flush=True)
+        y = tq2.gate_up_swiglu(soa, soa, _dev(x), n, k)
+        torch.cuda.synchronize()
+        got = y[:, idx].cpu().numpy()
+        del y
+        path = tq2.gemm_path(m, n, k)
+        ref, e = oracle.swiglu_from_parts(
+            oracle.gate_up_swiglu_parts(aos_rows, aos_rows, x, len(rows), k), TOL[path])
+        ok, msg = check_swiglu(got, ref, e, path, "largest swiglu m=%d" % m)
         print(msg, flush=True)
         assert ok, msg
 
@@ -480,7 +502,6 @@ def test_gemm_precise_config4(tq2):
 # tq2_gate_up_swiglu: silu(x W_gate^T) * (x W_up^T), both projections fused.
 # ---------------------------------------------------------------------------
 
-from tests.parity import check_swiglu  # noqa: E402
 
 
 def run_swiglu(tq2, case):
