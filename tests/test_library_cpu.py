@@ -244,3 +244,24 @@ def test_binding_requires_one_device():
     assert tq2._one_device(("x", a), ("residual", None), ("out", a)) == a.device
     with pytest.raises(ValueError, match="out is on meta"):
         tq2._one_device(("x", a), ("out", b))
+
+
+def test_binding_mirrors_the_header():
+    """The binding's status codes, batch limit and problem struct are the
+    header's: values parsed from include/tq2.h, fields in declaration order
+    with the same sizes (pointers and int64_t, no padding)."""
+    with open(os.path.join(ROOT, "include", "tq2.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    codes = dict((k, int(v)) for k, v in re.findall(r"\b(TQ2_(?:OK|ERR_[A-Z]+))\s*=\s*(-?\d+)", text))
+    assert len(codes) == 7
+    for name, value in codes.items():
+        assert getattr(tq2, name) == value, name
+    assert int(re.search(r"#define\s+TQ2_GEMV_BATCH_MAX\s+(\d+)", text).group(1)) == \
+        tq2.GEMV_BATCH_MAX
+    body = re.search(r"typedef struct tq2_gemv_problem \{(.*?)\}", text, flags=re.S).group(1)
+    fields = re.findall(r"(\w+)\s*;", body)
+    assert fields == [f[0] for f in tq2.GemvProblem._fields_]
+    sizes = {"soa": 8, "x": 8, "residual": 8, "out": 8, "n": 8, "k": 8}
+    for name, ctype in tq2.GemvProblem._fields_:
+        assert ctypes.sizeof(ctype) == sizes[name], name
+    assert ctypes.sizeof(tq2.GemvProblem) == 48
