@@ -10,6 +10,11 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// Cache policy operand of a buffer load for data that one launch reads once
+// (a weight streamed by the decode kernels): the non-temporal hint, so the
+// stream is not kept in the caches at the expense of reused data (x).
+constexpr int kStreamOnce = 2;
+
 // Raw buffer resource over `bytes` bytes at `base`: a load whose per-lane
 // offset (plus the instruction offset) reaches past the end returns zeros.
 // The hardware range check does not include the scalar offset operand, so a

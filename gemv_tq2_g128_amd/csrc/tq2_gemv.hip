@@ -126,9 +126,9 @@ template <Fmt F>
 __device__ __forceinline__ uint32_t unit_word_at(rsrc_t rc, uint32_t lane_row_off,
                                                  uint32_t row_off, unsigned u) {
   if constexpr (F == Fmt::kQ1)
-    return __builtin_amdgcn_raw_buffer_load_b32(rc, lane_row_off + (u >> 1) * 4u, row_off, 0) >>
-           (8 * (u & 1));
-  return __builtin_amdgcn_raw_buffer_load_b32(rc, lane_row_off + u * 4u, row_off, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(rc, lane_row_off + (u >> 1) * 4u, row_off,
+                                                kStreamOnce) >> (8 * (u & 1));
+  return __builtin_amdgcn_raw_buffer_load_b32(rc, lane_row_off + u * 4u, row_off, kStreamOnce);
 }
 
 // Row `r` of a block whose first row is blk_row0, as an index into the
@@ -142,7 +142,8 @@ __device__ __forceinline__ uint32_t block_row(int blk_row0, int r, int n_rows) {
   return uint32_t(r);
 }
 
-// Code word and scale of lane unit u of block row `row`.  SLOTS == 1: the
+// Code word and scale of lane unit u of block row `row`, loaded as a stream
+// read once per launch (kStreamOnce).  SLOTS == 1: the
 // row's offset is a scalar (the scalar offset operand) and the lane's offset
 // is the same for every row, so a row costs no vector address arithmetic.
 template <int SLOTS, Fmt F>
@@ -151,10 +152,12 @@ __device__ __forceinline__ void load_row(rsrc_t rc, rsrc_t rs, uint32_t row, uin
                                          uint32_t& db) {
   if constexpr (SLOTS == 1) {
     cw = unit_word_at<F>(rc, 0u, row * wrow * 4u, u);
-    db = __builtin_amdgcn_raw_buffer_load_b16(rs, (u >> 3) * 2u, row * kb_count * 2u, 0);
+    db = __builtin_amdgcn_raw_buffer_load_b16(rs, (u >> 3) * 2u, row * kb_count * 2u,
+                                              kStreamOnce);
   } else {
     cw = unit_word_at<F>(rc, row * wrow * 4u, 0u, u);
-    db = __builtin_amdgcn_raw_buffer_load_b16(rs, (row * kb_count + (u >> 3)) * 2u, 0, 0);
+    db = __builtin_amdgcn_raw_buffer_load_b16(rs, (row * kb_count + (u >> 3)) * 2u, 0,
+                                              kStreamOnce);
   }
 }
 
