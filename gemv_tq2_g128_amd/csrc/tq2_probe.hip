@@ -12,7 +12,8 @@ namespace {
 constexpr int kProbeThreads = 256;
 
 // Grid-stride read of n16 16-byte words, four independent (guarded) loads in
-// flight per thread per step.  The words are folded into one value per
+// flight per thread per step, with the non-temporal hint (the fastest plain
+// read of a stream touched once, as the decode GEMV's weight loads are).  The words are folded into one value per
 // thread, stored only if it equals a constant the data never has to match,
 // so the loads cannot be dropped and almost nothing is written.
 __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* __restrict__ p,
@@ -21,11 +22,17 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const uint4* 
   uint32_t acc = 0;
   const size_t stride = size_t(gridDim.x) * kProbeThreads;
   for (size_t i = size_t(blockIdx.x) * kProbeThreads + threadIdx.x; i < n16; i += 4 * stride) {
+    typedef unsigned int ntv4 __attribute__((ext_vector_type(4)));
     uint4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const size_t idx = i + size_t(j) * stride;
-      v[j] = idx < n16 ? p[idx] : make_uint4(0u, 0u, 0u, 0u);
+      if (idx < n16) {
+        const ntv4 t = __builtin_nontemporal_load(reinterpret_cast<const ntv4*>(p) + idx);
+        v[j] = make_uint4(t[0], t[1], t[2], t[3]);
+      } else {
+        v[j] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
