@@ -7,6 +7,10 @@ as achieved HBM GB/s of algorithmic bytes (codes + scales + x + residual +
 out, each counted once).  The weight of every call comes from a pool of
 copies larger than the 256 MB Infinity Cache, so each call streams its
 weight from HBM; the calls are replayed back to back from a HIP graph.
+Every timed region (the headline's exactly --steps calls after exactly
+--warmup untimed ones) is preceded by an untimed run-in of the same calls,
+about 20 ms of GPU time, so that it measures them at the clock the GPU
+settles to under that load rather than at the idle clock (time_graphs).
 
 Also reported in the same line: the roofline object of the dominant kernel,
 the CPU oracle's throughput on a bounded sample of the same workload, and the
@@ -116,26 +120,139 @@ def run_environment(torch):
     return env
 
 
+def _sclk_file(torch):
+    """The driver's pp_dpm_sclk file of the GPU torch calls cuda:0 (matched
+    by PCI address), else the first one found, or None."""
+    import glob
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    props = torch.cuda.get_device_properties(0)
+    bus = getattr(props, "pci_bus_id", None)
+    if bus is not None:
+        want = "%04x:%02x:%02x" % (getattr(props, "pci_domain_id", 0), bus,
+                                   getattr(props, "pci_device_id", 0))
+        for f in files:
+            if os.path.basename(os.path.realpath(os.path.dirname(f))).startswith(want):
+                return f
+    return files[0] if files else None
+
+
+class ClockSampler:
+    """Samples the GFX clock level the driver marks as current ('*' in
+    pp_dpm_sclk) from a background thread, about once a millisecond, while
+    `with sampler.phase(name):` blocks run; reports MHz per phase."""
+
+    def __init__(self, torch):
+        import threading
+        self.path = _sclk_file(torch)
+        self.samples = {}
+        self._name = None
+        self._stop = threading.Event()
+        self._thread = None
+        if self.path:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def _read(self):
+        import re
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.wait(0.001):
+            name = self._name
+            if name is not None:
+                mhz = self._read()
+                if mhz is not None:
+                    self.samples.setdefault(name, []).append(mhz)
+
+    def phase(self, name):
+        sampler = self
+
+        class _Phase:
+            def __enter__(self):
+                sampler._name = name
+
+            def __exit__(self, *exc):
+                sampler._name = None
+        return _Phase()
+
+    def report(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=1.0)
+        out = {"source": self.path}
+        for name, v in self.samples.items():
+            v = sorted(v)
+            out[name] = {"samples": len(v), "min_mhz": v[0], "median_mhz": v[len(v) // 2],
+                         "max_mhz": v[-1]}
+        return out
+
+
 def gemv_bytes(n, k, residual):
     codes_scales = n * (k // 128) * 34
     return codes_scales + 4 * k + 4 * n + (4 * n if residual else 0)
 
 
-def time_graph(torch, graph, replays, stream):
-    """Replay a captured graph ``replays`` times between two events on the
-    stream the kernels run on; returns (event ms, wall s)."""
+# Untimed run-in ahead of every timed region.  The GPU's clock governor
+# takes milliseconds of load to leave the level it idles at (a 20-call GEMV
+# region that starts from idle runs at 650-700 MHz, against 1.4-1.6 GHz once
+# the same calls have run for a while), so each region is preceded by about
+# SETTLE_MS of the same calls, untimed; the region then measures the calls at
+# the clock they settle to.
+SETTLE_MS = 20.0
+
+
+def _replay(graphs):
+    for graph, replays in graphs:
+        for _ in range(replays):
+            graph.replay()
+
+
+def time_graphs(torch, graphs, stream, warm=()):
+    """Time [(graph, replays)] back to back on `stream` with two events.
+
+    Enqueued with no synchronisation in between: a run-in of the timed graphs
+    themselves (passes over them until about SETTLE_MS of GPU time, from one
+    untimed pass measured beforehand), the untimed `warm` [(graph, replays)],
+    the start event, the timed replays and the end event.  The run-in keeps
+    the stream busy while the host submits the rest, so the region holds
+    exactly the timed calls, at the clock the workload settles to, and not the
+    host's submission of them.  Returns (event ms, wall s of the region's
+    submission and execution)."""
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         start.record(stream)
-        for _ in range(replays):
-            graph.replay()
+        _replay(graphs)
         end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return start.elapsed_time(end), wall
+    passes = max(1, min(2000, int(math.ceil(SETTLE_MS / max(start.elapsed_time(end), 1e-3)))))
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        for _ in range(passes):
+            _replay(graphs)
+        _replay(warm)
+        t0 = time.perf_counter()
+        start.record(stream)
+        _replay(graphs)
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), time.perf_counter() - t0
+
+
+def time_graph(torch, graph, replays, stream):
+    """`replays` timed replays of one graph, after one untimed replay of it
+    (see time_graphs); returns (event ms, wall s)."""
+    return time_graphs(torch, [(graph, replays)], stream, warm=[(graph, 1)])
 
 
 def capture(torch, stream, fn, count):
@@ -163,39 +280,82 @@ def exact_graphs(torch, stream, fn, calls, chunk=2048):
     return out
 
 
-def time_graphs(torch, graphs, stream):
-    """Replay [(graph, replays)] back to back between two events on the stream
-    the kernels run on; returns (event ms, wall s)."""
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        for graph, replays in graphs:
-            for _ in range(replays):
-                graph.replay()
-        end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end), time.perf_counter() - t0
+def _time_oracle(fn, seconds):
+    """Evaluations of fn() for about `seconds` (at least one; an untimed
+    call first when seconds > 0); returns (evaluations, seconds per
+    evaluation)."""
+    if seconds > 0:
+        fn()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return reps, dt / reps
 
 
-def cpu_baseline(case, seconds):
-    """The oracle as it stands, on the host, single BLAS thread."""
+def cpu_baseline(case2, seconds):
+    """The oracle as it stands (float64 NumPy dequantise + product), on the
+    host, per workload, with 1 BLAS thread and with the host's cores.
+
+    The dequantisation is single-threaded NumPy; the BLAS threads speed up
+    only the float64 product.  Workloads: the two GEMVs in full; the
+    small-batch prefill at M = 8 and M = 100 in full; the M = 1536 GEMM in
+    full; the 100-layer chain on 64 output columns per layer (every layer's
+    first 64 weight rows against fixed N(0, 1) inputs: the chain input for
+    K = 3072, a seeded draw for K = 12288).  The headline `value` is the
+    K = N = 4096 residual GEMV at the host's cores, in the headline's
+    unit."""
     from threadpoolctl import threadpool_limits
+    import numpy as np
     import oracle
-    n, k = case["n"], case["k"]
-    nbytes = gemv_bytes(n, k, case["residual"] is not None)
-    with threadpool_limits(limits=1):
-        oracle.matmul(case["aos"], case["x"], n, k, case["residual"])    # warm
-        reps, t0 = 0, time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            oracle.matmul(case["aos"], case["x"], n, k, case["residual"])
-            reps += 1
-        dt = (time.perf_counter() - t0) / reps
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    import tq2_inputs as G
+    cores = len(os.sched_getaffinity(0))
+    c1, c3_8, c3_100, c4 = G.config1(), G.config3(8), G.config3(100), G.config4()
+    chain_x = {3072: G.chain_input(),
+               12288: G.make_activations(np.random.default_rng(12288), G.CHAIN_M, 12288)}
+    chain_w = [G.chain_layer_weight(layer) for layer in range(G.CHAIN_LAYERS)]
+    cols = np.arange(64)
+
+    def full(c):
+        return lambda: oracle.matmul(c["aos"], c["x"], c["n"], c["k"], c["residual"])
+
+    def chain():
+        for layer, w in enumerate(chain_w):
+            k, n = G.chain_layer_shape(layer)
+            oracle.matmul_rows(w, chain_x[k], n, k, cols)
+
+    chain_flop = sum(2.0 * G.CHAIN_M * 64 * G.chain_layer_shape(l)[0]
+                     for l in range(G.CHAIN_LAYERS))
+    legs = [
+        ("gemv_m1_k1024_n1024", full(c1), gemv_bytes(1024, 1024, False), "GB/s", seconds / 8),
+        ("gemv_m1_k4096_n4096_residual", full(case2), gemv_bytes(4096, 4096, True), "GB/s",
+         seconds / 4),
+        ("gemm_m8_k4096_n11008", full(c3_8), 2.0 * 8 * 11008 * 4096, "GFLOP/s", 0.0),
+        ("gemm_m100_k4096_n11008", full(c3_100), 2.0 * 100 * 11008 * 4096, "GFLOP/s", 0.0),
+        ("gemm_m1536_k3072_n3072", full(c4), 2.0 * 1536 * 3072 * 3072, "GFLOP/s", seconds / 8),
+        ("chain_100_layers_m1536_64_columns_per_layer", chain, chain_flop, "GFLOP/s", 0.0),
+    ]
+    per = {}
+    for name, fn, work, unit, secs in legs:
+        per[name] = {}
+        for threads in ((1, cores) if cores > 1 else (1,)):
+            if name.startswith("chain") and threads == 1 and cores > 1:
+                continue                         # about 5 s per pass: host cores only
+            with threadpool_limits(limits=threads):
+                reps, dt = _time_oracle(fn, secs)
+            per[name]["threads_%d" % threads] = {
+                "value": round(work / dt / 1e9, 4), "unit": unit, "s_per_eval": round(dt, 4),
+                "evals": reps}
+    head = per["gemv_m1_k4096_n4096_residual"]["threads_%d" % cores]
+    return {"value": head["value"], "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": "%d full oracle evaluations of the K=N=4096 residual GEMV (float64 numpy "
-                      "dequantize + product, 1 BLAS thread), %.3f s each" % (reps, dt)}
+                      "dequantise, single-threaded, + product with %d BLAS threads), %.3f s "
+                      "each; per-workload figures at 1 thread and %d threads in `workloads` "
+                      "(the chain on 64 output columns per layer)" %
+                      (head["evals"], cores, head["s_per_eval"], cores),
+            "workloads": per}
 
 
 def chain_bench(torch, tq2, G, dev, stream):
@@ -345,11 +505,73 @@ def launch_floor(torch, dev, stream, base, pool, sb, blocks, steps):
 
     out = {"grid": "%d blocks x 256 threads" % blocks, "read_bytes": sb, "calls": steps}
     for name, fn in (("empty", empty_call), ("read", read_call)):
-        time_graphs(torch, exact_graphs(torch, stream, fn, min(steps, 512)), stream)
-        ms, _ = time_graphs(torch, exact_graphs(torch, stream, fn, steps), stream)
+        warm = exact_graphs(torch, stream, fn, min(steps, 512))
+        ms, _ = time_graphs(torch, exact_graphs(torch, stream, fn, steps), stream, warm=warm)
         out[name + "_us_per_launch"] = round(ms * 1e3 / steps, 3)
     out["read_gbs"] = round(sb / (out["read_us_per_launch"] * 1e-6) / 1e9, 2)
     return out
+
+
+def gemm_shape_bench(torch, tq2, G, dev, stream, m, n, k, args):
+    """tq2_gemm at one shape with config 4's distributions (codes uniform over
+    {-1, 0, +1}, d ~ U[0.01, 0.1], x ~ N(0, 1) with 1% outliers x20; seed
+    from the shape), graph-replayed back to back: TFLOP/s."""
+    import numpy as np
+    rng = np.random.default_rng(m + 7 * n + 13 * k)
+    soa = tq2.reformat_aos_to_soa(torch.from_numpy(G.make_weight(rng, n, k)).to(dev), n, k)
+    x = torch.from_numpy(G.make_activations(rng, m, k, outlier_frac=0.01)).to(dev)
+    out = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+    def call(i):
+        st = tq2.gemm_ptr(soa.data_ptr(), x.data_ptr(), 0, out.data_ptr(), m, n, k,
+                          torch.cuda.current_stream(dev).cuda_stream)
+        if st != 0:
+            raise RuntimeError("tq2_gemm failed: %s" % tq2.status_string(st))
+
+    per_graph = 10
+    g = capture(torch, stream, call, per_graph)
+    reps = max(1, args.gemm_reps // 40)
+    ms, _ = time_graph(torch, g, reps, stream)
+    us = ms * 1e3 / (reps * per_graph)
+    tflops = 2.0 * m * n * k / (us * 1e-6) / 1e12
+    del g, soa, x, out
+    return {"tflops": round(tflops, 2), "us_per_call": round(us, 3),
+            "peak_tflops": F16_MFMA_PEAK_TFLOPS, "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
+            "path": tq2.gemm_path(m, n, k), "calls": reps * per_graph}
+
+
+def config1_bench(torch, tq2, G, dev, stream, args):
+    """The small decode GEMV, M = 1, K = N = 1024 (8192 blocks, 286,720
+    algorithmic bytes), weight copies rotated past the Infinity Cache, calls
+    replayed back to back; at this size one call is mostly launch cost."""
+    c = G.config1()
+    n, k = c["n"], c["k"]
+    soa = tq2.reformat_aos_to_soa(torch.from_numpy(c["aos"]).to(dev), n, k)
+    sb = tq2.soa_bytes(n, k)
+    pool = max(2, int(math.ceil(args.pool_mib * 2 ** 20 / sb)))
+    buf = soa.repeat(pool)
+    del soa
+    base = buf.data_ptr()
+    x = torch.from_numpy(c["x"]).to(dev).reshape(-1)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+
+    def call(i):
+        st = tq2.gemv_ptr(base + (i % pool) * sb, x.data_ptr(), 0, out.data_ptr(), n, k,
+                          torch.cuda.current_stream(dev).cuda_stream)
+        if st != 0:
+            raise RuntimeError("tq2_gemv failed: %s" % tq2.status_string(st))
+
+    calls = max(1, args.steps)
+    warm = exact_graphs(torch, stream, call, min(calls, 512))
+    ms, _ = time_graphs(torch, exact_graphs(torch, stream, call, calls), stream, warm=warm)
+    us = ms * 1e3 / calls
+    nbytes = gemv_bytes(n, k, False)
+    del buf
+    return {"gemv_m1_k1024_n1024": {
+        "us_per_call": round(us, 3), "bytes_per_call": nbytes,
+        "gbs": round(nbytes / (us * 1e-6) / 1e9, 2),
+        "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "copies_rotated": pool, "calls": calls}}
 
 
 def gemv_sweep(torch, tq2, G, dev, stream, args):
@@ -514,6 +736,7 @@ def main():
         return 1
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(dev)
+    clock = ClockSampler(torch)
 
     # ---- decode GEMV, K = N = 4096, fused residual -------------------------
     case = G.config2(with_residual=True)
@@ -537,14 +760,14 @@ def main():
 
     # Exactly `warmup` untimed calls, then exactly `steps` timed ones; call i
     # reads weight copy i % pool, so consecutive calls read different copies.
+    # The warm-up calls run right before the start event, with the timed calls
+    # already queued behind them (time_graphs).
     steps, warmup = max(1, args.steps), max(0, args.warmup)
-    if warmup:
-        warm = exact_graphs(torch, stream, gemv_call, warmup)
-        time_graphs(torch, warm, stream)
-        del warm
+    warm = exact_graphs(torch, stream, gemv_call, warmup) if warmup else []
     timed = exact_graphs(torch, stream, gemv_call, steps)
-    ms, wall = time_graphs(torch, timed, stream)
-    del timed
+    with clock.phase("headline_gemv"):
+        ms, wall = time_graphs(torch, timed, stream, warm=warm)
+    del timed, warm
     us_per_call = ms * 1e3 / steps
     gbs = nbytes / (us_per_call * 1e-6) / 1e9
 
@@ -636,6 +859,10 @@ def main():
             if st != 0:
                 raise RuntimeError("tq2_gemm_precise failed: %s" % tq2.status_string(st))
 
+        # The clock level during a long run of the same calls (about 100 ms;
+        # the timed region above is too short to sample).
+        with clock.phase("gemm_m1536_k3072_n3072"):
+            time_graph(torch, g4, max(1, int(0.1 / (us4 * 1e-6) / per_graph)), stream)
         gp = capture(torch, stream, precise_call, per_graph)
         time_graph(torch, gp, 1, stream)
         msp, _ = time_graph(torch, gp, max(1, reps // 2), stream)
@@ -643,12 +870,16 @@ def main():
         result["gemm_precise_m1536_k3072_n3072"] = {
             "tflops": round(2.0 * m4 * n4 * k4 / (usp * 1e-6) / 1e12, 2),
             "us_per_call": round(usp, 3), "path": 1, "tolerance": "1e-5 * sum|x w|"}
+        result["gemm_m1536_k16384_n3072"] = gemm_shape_bench(torch, tq2, G, dev, stream,
+                                                             1536, 3072, 16384, args)
         result["gemm_m1536_k3072_n3072"] = {
             "tflops": round(tflops, 2), "us_per_call": round(us4, 3),
             "peak_tflops": F16_MFMA_PEAK_TFLOPS, "frac": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
             "path": tq2.gemm_path(m4, n4, k4), "calls": reps * per_graph,
             "traffic": measured_traffic("gemm_traffic_bytes_per_launch",
                                         "gemv_tq2_g128_amd/csrc/tq2_gemm.hip")}
+
+    result.update(config1_bench(torch, tq2, G, dev, stream, args))
 
     if not args.no_sweep:
         result.update(gemv_sweep(torch, tq2, G, dev, stream, args))
@@ -663,7 +894,8 @@ def main():
         result.update(q1_bench(torch, tq2, G, dev, stream, args))
 
     if not args.no_chain:
-        result["chain_100_layers_m1536"] = chain_bench(torch, tq2, G, dev, stream)
+        with clock.phase("chain_100_layers_m1536"):
+            result["chain_100_layers_m1536"] = chain_bench(torch, tq2, G, dev, stream)
 
     if args.calibrate_copy_mib > 0:
         nb = args.calibrate_copy_mib * 2 ** 20
@@ -678,6 +910,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
 
     result["environment"] = run_environment(torch)
+    result["environment"]["gfx_clock_in_use"] = clock.report()
 
     print(json.dumps(result), flush=True)
     return 0

@@ -56,7 +56,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kChunk = 256;            // k per pipeline stage
 constexpr int kLdsRow = kChunk + 8;    // binary16 per LDS row (16-byte pad vs bank conflicts)
-constexpr int kPpMaxKB = 96;           // scale blocks per row the ping-pong kernel keeps in LDS (K <= 12288)
+constexpr int kPpMaxKB = 96;           // scale blocks per row the ping-pong kernel can keep in LDS (K <= 12288)
 
 __device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
@@ -632,7 +632,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 
   const uint32_t magic = 0x64006400u;
   const int npass = (K + PASS_K - 1) / PASS_K;
-  int e_acc = 0;                         // acc holds the sums times 2^e_acc
+  // acc holds the sums times 2^e_acc.  e_acc is a running exponent: the
+  // prescale_exponent of the largest |x| the wave has seen so far (passes of
+  // zeros leave it alone), so it only falls and acc is only ever scaled down.
+  int e_acc = 1 << 20;
   for (int pass = 0; pass < npass; ++pass) {
     const int k0 = pass * PASS_K + wave * SLICE;
     if (k0 >= K) break;                  // wave-uniform: the rest of K is past the end
@@ -678,9 +681,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 
     // ---- x fragments: hi = binary16(x 2^e) (RNE), lo = binary16(x 2^e - hi) --
     // Positions past K are zeroed (a partial last slice).  One power of two
-    // 2^e per wave and pass (prescale_exponent of the slice's largest |x|
-    // over all rows) scales x before the split; acc is kept at the scale of
-    // the current pass and brought to it from the previous pass's.
+    // 2^e per wave and pass scales x before the split: e is the running
+    // exponent, lowered to the prescale_exponent of this slice's largest |x|
+    // (over all rows) when that is smaller; acc is brought down to it.
     float mx = 0.f;
 #pragma unroll
     for (int h = 0; h < CPW; ++h) {
@@ -693,8 +696,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
       }
       mx = fmaxf(mx, live ? mh : 0.f);
     }
-    const int e = prescale_exponent(wave_max_nonneg(mx));
-    if (pass > 0) {                      // acc from the previous pass's scale to this one's
+    const float mr = wave_max_nonneg(mx);
+    const int e = mr > 0.f ? min(e_acc, prescale_exponent(mr)) : e_acc;
+    if (e != e_acc) {                    // wave-uniform; acc only ever scaled down
 #pragma unroll
       for (int t = 0; t < TMAX; ++t)
 #pragma unroll
@@ -853,7 +857,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 //
 // SWIGLU: waves wn = 0, 1 of each group read gate-weight columns, waves 2, 3
 // the same columns of the up weight; the output tile is MT x 2NW.
-template <int MT, int NW, bool SWIGLU, Fmt F>
+//
+// Scales.  LDS_SCALES (K <= 12288): the block's scales for the whole K are
+// loaded into LDS once, before the loop.  Otherwise group 0 loads each
+// chunk's scales with its code words and hands group 1's copy over through
+// LDS with them; the per-chunk gathers cost about 10% at K <= 12288, so they
+// serve only the K the LDS copy cannot hold.
+template <int MT, int NW, bool SWIGLU, Fmt F, bool LDS_SCALES>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
@@ -872,10 +882,10 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   static_assert((MT / 2) * (kChunk / 4) % GT == 0, "x staging split");
 
   __shared__ _Float16 As[2][MT][kLdsRow];
-  // The block's scales for the whole K (NT rows of the scales plane, which
-  // are contiguous; with SWIGLU 2NW gate rows, then the same 2NW up rows),
-  // loaded once.
-  __shared__ __attribute__((aligned(16))) uint16_t Ls[NT * kPpMaxKB];
+  // LDS_SCALES: the block's scales for the whole K (NT rows of the scales
+  // plane, which are contiguous; with SWIGLU 2NW gate rows, then the same 2NW
+  // up rows), loaded once.
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[LDS_SCALES ? NT * kPpMaxKB : 8];
 
   const int ntiles = tiles_m * tiles_n;
   int t = blockIdx.x;
@@ -902,6 +912,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   const rsrc_t rx = make_rsrc(x + size_t(m0) * K, uint32_t(min(MT, M - m0)) * uint32_t(K) * 4u);
   const uint32_t row_bytes = uint32_t(K / 8) * uint32_t(BITS);   // codes per weight row
   const rsrc_t rc = make_rsrc(upw ? ucodes : codes, uint32_t(N) * row_bytes);
+  const rsrc_t rs = make_rsrc(upw ? uscales : scales, uint32_t(N) * uint32_t(KB) * 2u);
 
   // x staging: group p converts rows p*MT/2 .. p*MT/2 + MT/2 - 1 of a chunk;
   // its thread gt handles float4 f = gt + GT*i: row f / 64, float4 f % 64.
@@ -929,13 +940,20 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
 
   // Weights: lane's column and k-group g.  Group 0 loads the code words of
   // both groups' halves of the steps (one 2*QW-dword load per column group,
-  // twice the bytes per instruction of a per-group load) and hands group 1's
-  // half over through LDS one phase later; group 1 issues no weight loads.
-  // cw[j][0 .. QW) is the calling group's half.
+  // twice the bytes per instruction of a per-group load), without LDS_SCALES
+  // also the raw binary16 scale of the block they fall in (block
+  // 2c + (g >> 1), the same for both halves), and hands group 1's half (and
+  // the scale) over through LDS one phase later; group 1 issues no weight
+  // loads.  cw[j][0 .. QW) is the calling group's half.  Columns past N read
+  // as zero codes and zero scales; chunks past the end read the next row's
+  // bytes, which the caller masks (decode_all zeroes d where k runs past K).
   const uint32_t nl = uint32_t(n0 + wc * NW + col);
   const uint32_t code_voff = nl * row_bytes + 8u * BITS * uint32_t(g);
+  const uint32_t scale_voff = (nl * uint32_t(KB) + uint32_t(g >> 1)) * 2u;
   uint32_t cw[CG][2 * QW];
+  uint32_t dsc[CG];                            // raw binary16 scale bits
   __shared__ uint32_t Hw[4 * CG * 64 * QW];    // hand-over: [wn][j][lane][QW]
+  __shared__ uint16_t Hd[LDS_SCALES ? 8 : 4 * CG * 64];   // scale hand-over: [wn][j][lane]
   auto load_w = [&](int c) {                   // group 0
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
@@ -947,6 +965,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
         const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
         cw[j][0] = v[0]; cw[j][1] = v[1];
       }
+      if constexpr (!LDS_SCALES)
+        dsc[j] = __builtin_amdgcn_raw_buffer_load_b16(
+            rs, scale_voff + uint32_t(j * 16 * KB * 2 + c * 4), 0, 0);
     }
   };
   auto hand_over = [&]() {                     // group 0: group 1's half into LDS
@@ -957,6 +978,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
         *reinterpret_cast<u32x2_t*>(h) = u32x2_t{cw[j][2], cw[j][3]};
       else
         *h = cw[j][1];
+      if constexpr (!LDS_SCALES) Hd[(wn * CG + j) * 64 + lane] = uint16_t(dsc[j]);
     }
   };
   auto take_over = [&]() {                     // group 1: its half from LDS
@@ -969,16 +991,18 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
       } else {
         cw[j][0] = *h;
       }
+      if constexpr (!LDS_SCALES) dsc[j] = Hd[(wn * CG + j) * 64 + lane];
     }
   };
-  // Scale of this lane's column j and chunk c: block 2c + (g >> 1).  The
-  // chunk is clamped so the read stays inside Ls for the pass past the end;
-  // with an odd block count the last chunk's second block reads the next
-  // row's first scale (still inside Ls, since KB < kPpMaxKB), and the caller
-  // zeroes it.
+  // LDS_SCALES: scale of this lane's column j and chunk c, block 2c + (g >> 1).
+  // The chunk is clamped so the read stays inside Ls for the pass past the
+  // end; with an odd block count the last chunk's second block reads the
+  // next row's first scale (still inside Ls, since KB < kPpMaxKB), and the
+  // caller zeroes it.
   const int ls_base = (wn * NW + col) * KB + (g >> 1);
-  auto scale_of = [&](int j, int c) {
-    return __builtin_bit_cast(_Float16, Ls[ls_base + j * 16 * KB + 2 * min(c, nchunks - 1)]);
+  auto scale_bits = [&](int j, int c) -> uint32_t {
+    if constexpr (LDS_SCALES) return Ls[ls_base + j * 16 * KB + 2 * min(c, nchunks - 1)];
+    return dsc[j];
   };
 
   // Decoded weight operands of one MFMA phase.  The memory phase decodes
@@ -993,7 +1017,8 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     const bool live = c * kChunk + 64 * g < K && c < nchunks;
 #pragma unroll
     for (int j = 0; j < CG; ++j) {
-      const _Float16 d = live ? scale_of(j, c) : _Float16(0.0f);
+      const _Float16 d =
+          live ? __builtin_bit_cast(_Float16, uint16_t(scale_bits(j, c))) : _Float16(0.0f);
       if constexpr (F == Fmt::kQ1) {
         // One word holds the four steps; dlast carries the |d| pair's bits.
         const uint32_t db = __builtin_bit_cast(uint16_t, d);
@@ -1109,11 +1134,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
     pin_operands();
   };
 
-  // Prologue: the block's scales into LDS; x tile 0 complete in buffer 0;
-  // group 0's operands for chunk 0 decoded, group 1's half of chunk 0 handed
-  // over, and weight chunk 1 in flight.  Both groups hold their half of x
-  // chunk 1 in registers.
-  {
+  // Prologue: (LDS_SCALES) the block's scales into LDS; x tile 0 complete in
+  // buffer 0; group 0's operands for chunk 0 decoded, group 1's half of
+  // chunk 0 (and its scales) handed over, and weight chunk 1 in flight.  Both
+  // groups hold their half of x chunk 1 in registers.
+  if constexpr (LDS_SCALES) {
     // 16-byte loads for the whole granules (a load that straddles the end
     // of a buffer resource returns zeros in full), 2-byte loads for the tail.
     // Entries for columns past N are left unset: their outputs are never
@@ -1144,7 +1169,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   if (grp == 0) load_w(0);
   store_a(0);
   load_a(1, 0, AV);
-  lds_barrier();                         // scales visible
+  lds_barrier();                         // LDS_SCALES: scales visible
   if (grp == 0) {
     decode_all(0);
     hand_over();
@@ -1237,7 +1262,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
 }
 
 // `up` is null for the plain matmul; with SWIGLU, `soa` is the gate weight.
-template <int MT, int NW, bool SWIGLU, Fmt F>
+template <int MT, int NW, bool SWIGLU, Fmt F, bool LDS_SCALES>
 hipError_t launch_pp(const uint8_t* soa, const uint8_t* up, const float* x,
                      const float* residual, float* out, int64_t m, int64_t n, int64_t k,
                      hipStream_t stream) {
@@ -1247,7 +1272,7 @@ hipError_t launch_pp(const uint8_t* soa, const uint8_t* up, const float* x,
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(unsigned(tm * tn));
   const size_t so = scales_offset(F, n, k);
-  hipLaunchKernelGGL((gemm_pp_kernel<MT, NW, SWIGLU, F>), grid, dim3(512), 0, stream, soa, soa + so,
+  hipLaunchKernelGGL((gemm_pp_kernel<MT, NW, SWIGLU, F, LDS_SCALES>), grid, dim3(512), 0, stream, soa, soa + so,
                      up, up ? up + so : nullptr, x, residual, out, int(m), int(n), int(k), int(tm),
                      int(tn));
   return hipGetLastError();
@@ -1334,8 +1359,8 @@ hipError_t dispatch(int path, const uint8_t* soa, const uint8_t* up, const float
     }
   }
   if (k <= int64_t(kPpMaxKB) * kBlockWeights)
-    return launch_pp<96, 48, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-  return launch_tile<96, 48, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+    return launch_pp<96, 48, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
+  return launch_pp<96, 48, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
 }
 
 }  // namespace

@@ -48,25 +48,52 @@
 extern "C" {
 #endif
 
+/* Status of a call.  Error policy of the pages (oxibonsai-image 0.2.2,
+ * src/gpu.rs: the module doc's last paragraph, the `GpuMatmulError` enum and
+ * the "# Errors" section of `ternary_matmul_gpu`): every failure of the GPU
+ * matmul -- device unavailable, weight upload / encode / dispatch failed,
+ * k % 128 != 0, a length mismatch -- comes back to the caller as a value, and
+ * nothing panics or aborts.  The codes split that enum's cases finer:
+ * GraphUnavailable is TQ2_ERR_DEVICE; the `Metal` case (encode / dispatch)
+ * is TQ2_ERR_LAUNCH; the argument errors its doc names are TQ2_ERR_SHAPE
+ * (k % 128 != 0) and TQ2_ERR_INVALID (a length or size the call cannot
+ * take).  TQ2_ERR_ALIGN and TQ2_ERR_ALIAS are this library's own checks of
+ * raw device pointers, which the pages' slice-typed API cannot receive.  The
+ * pages' caller turns any error into a CPU fallback; this library has none,
+ * so the caller sees the status. */
 typedef enum tq2_status {
   TQ2_OK = 0,
-  TQ2_ERR_INVALID = -1, /* null pointer, negative size, K <= 0, size too large */
-  TQ2_ERR_SHAPE = -2,   /* K is not a multiple of 128 (gpu.rs: `ternary_matmul_gpu` errors) */
+  TQ2_ERR_INVALID = -1, /* null pointer, negative size, K <= 0, size too large (gpu.rs,
+                           `ternary_matmul_gpu` "# Errors": a length the call cannot take) */
+  TQ2_ERR_SHAPE = -2,   /* K is not a multiple of 128 (gpu.rs, `ternary_matmul_gpu`
+                           "# Errors": `k % 128 != 0`) */
   TQ2_ERR_ALIGN = -3,   /* soa not 256-byte aligned, or x / out / residual not 16-byte aligned */
   TQ2_ERR_ALIAS = -4,   /* out overlaps x or soa, residual partially overlaps out, aos overlaps soa */
-  TQ2_ERR_DEVICE = -5,  /* current HIP device is not gfx950, or HIP could not be queried */
-  TQ2_ERR_LAUNCH = -6   /* the kernel launch failed */
+  TQ2_ERR_DEVICE = -5,  /* current HIP device is not gfx950, or HIP could not be queried
+                           (gpu.rs, `GpuMatmulError::GraphUnavailable`: no usable device) */
+  TQ2_ERR_LAUNCH = -6   /* the kernel launch failed (gpu.rs, `GpuMatmulError::Metal`:
+                           encode / dispatch failed) */
 } tq2_status;
 
-/* Bytes of an [n, k] weight in the 34-byte AoS block format: n * (k/128) * 34.
- * Returns 0 for n < 0, k <= 0 or k % 128 != 0. */
+/* Bytes of an [n, k] weight in the 34-byte AoS block format: n * (k/128) * 34,
+ * the byte length of the blocks' raw view that gpu.rs uploads (oxibonsai-image
+ * 0.2.2, src/gpu.rs: doc of `blocks_as_bytes`, a `#[repr(C)]` 34-byte block
+ * `qs[32]` then the binary16 `d`, and its test that the view is 34 bytes per
+ * block; `ternary_matmul_gpu` takes n * (k / 128) blocks).
+ * Returns 0 for n < 0, k <= 0 or k % 128 != 0.  Pure host function. */
 size_t tq2_aos_bytes(int64_t n, int64_t k);
 
-/* Bytes the library's resident SoA copy of an [n, k] weight occupies
- * (a multiple of 256).  Returns 0 for invalid n, k as above. */
+/* Bytes the library's resident SoA copy of an [n, k] weight occupies (a
+ * multiple of 256): the buffer `reformat_tq2_aos_to_soa` fills from the AoS
+ * bytes and the matmul keeps resident (gpu.rs: doc of `blocks_as_bytes`, and
+ * `ternary_matmul_gpu`'s "resident SoA buffer").  2.125 bits per weight, as
+ * the AoS.  Returns 0 for invalid n, k as above.  Pure host function. */
 size_t tq2_soa_bytes(int64_t n, int64_t k);
 
-/* Version number of the private SoA layout written by tq2_reformat_aos_to_soa. */
+/* Version number of the private SoA layout written by tq2_reformat_aos_to_soa
+ * (the pages' kernels likewise share one private SoA weight buffer:
+ * oxibonsai-kernels 0.1.5, pipelines.rs, fields `gemm_tq2_g128_v9_simdgroup`
+ * and `gemm_tq2_g128_v10_simdgroup`, "same op / SoA weight buffer"). */
 int tq2_soa_layout_version(void);
 
 /* Convert an [n, k] weight from AoS blocks (`aos`, tq2_aos_bytes(n, k) bytes,
@@ -125,11 +152,13 @@ int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream);
  *   0: M == 1, the GEMV above;
  *   1: 2 <= M <= 16: matrix-core GEMM with x split into two binary16 parts
  *      (x = hi + lo), error within 1e-5 * sum|x w| at any magnitude of x:
- *      each wave scales its 4096-wide K slice of x by a power of two before
- *      the split so that both parts stay normal binary16, and scales the sums
- *      back (exact); an element more than 2^17 times smaller than the largest
- *      |x| of its slice (over the rows the wave holds) keeps an absolute error
- *      below 2^-39 of that largest |x|;
+ *      each wave scales its slice of x (per 4096-wide pass over K) by a power
+ *      of two before the split so that both parts stay normal binary16, and
+ *      scales the sums back (exact); the power follows the largest |x| the
+ *      wave has seen so far (over the rows it holds, in this and earlier
+ *      passes), so it only falls and the sums never overflow; an element more
+ *      than 2^17 times smaller than that largest |x| keeps an absolute error
+ *      below 2^-39 of it;
  *   2: M > 16: matrix-core GEMM with x rounded to binary16 and weights staged
  *      as exact binary16 code * d (oxibonsai-kernels 0.1.5, pipelines.rs,
  *      fields `gemm_tq2_g128_v9_simdgroup` / `gemm_tq2_g128_v10_simdgroup`:
@@ -220,10 +249,23 @@ int tq2_q1_gate_up_swiglu(const void* gate_soa, const void* up_soa, const float*
                           int64_t m, int64_t n, int64_t k, void* stream);
 
 /* The kernel tq2_gemm uses for this shape (0, 1 or 2 as listed above), or
- * TQ2_ERR_INVALID / TQ2_ERR_SHAPE for an invalid shape.  Pure host function. */
+ * TQ2_ERR_INVALID / TQ2_ERR_SHAPE for an invalid shape.  Pure host function.
+ * The pages pick among their ternary kernels inside `encode_gemm_tq2`
+ * (oxibonsai-kernels 0.1.5, pipelines.rs, `MetalPipelines` fields
+ * `gemm_tq2_g128_v8_tiled`, `gemm_tq2_g128_v9_simdgroup` and
+ * `gemm_tq2_g128_v10_simdgroup`: the large-M path dispatches the
+ * matrix-unit kernel, and v10 only when it passes parity and is faster), and
+ * gpu.rs reports only whether the GPU ran at all (`gpu_was_used`, the
+ * `GPU_USED` flag used to prove the GPU path executed).  This query states the
+ * choice before the call, as a pure function of the shape, so a caller (or a
+ * test) knows which kernel -- and so which accuracy bound above -- applies. */
 int tq2_gemm_path(int64_t m, int64_t n, int64_t k);
 
-/* Static description of a status value ("ok", "invalid argument", ...). */
+/* Static description of a status value ("ok", "invalid argument", ...): the
+ * counterpart of the `#[error(...)]` messages of gpu.rs's `GpuMatmulError`
+ * (oxibonsai-image 0.2.2, src/gpu.rs), for callers that log a failure
+ * instead of panicking.  Unknown values give "unknown tq2 status"; the
+ * returned string is static and must not be freed. */
 const char* tq2_status_string(int status);
 
 #ifdef __cplusplus

@@ -181,7 +181,8 @@ def test_gemv_shapes(tq2, n, k):
 GEMM_SHAPES = [(2, 17, 128), (3, 100, 384), (8, 64, 256), (15, 65, 640), (16, 257, 1024),
                (17, 200, 384), (31, 33, 128), (32, 300, 512), (33, 100, 256), (64, 129, 384),
                (65, 64, 1024), (96, 192, 256), (97, 250, 640), (128, 300, 512),
-               (129, 191, 384), (200, 385, 768), (300, 1000, 1152)]
+               (129, 191, 384), (200, 385, 768), (300, 1000, 1152), (150, 50, 12416),
+               (257, 200, 16512)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
@@ -308,6 +309,52 @@ def test_skinny_passes_with_different_scales(tq2, m):
     c["x"] = x
     c["name"] = "skinny_pass_scales_m%d" % m
     assert_case(tq2, c)
+
+
+@pytest.mark.parametrize("m", [3, 8, 12, 40])
+def test_split_paths_falling_then_rising_magnitude(tq2, m):
+    """K = 12416: x about 1e16 in the first 4096-wide pass, 1e-16 in the
+    second and 1 in the rest.  The split kernels' power of two only falls (it
+    follows the largest |x| seen so far), so the large first pass is not
+    scaled up past the f32 range when the tiny second pass arrives; the
+    result is within 1e-5 * S, S dominated by the first pass.  M <= 16 runs
+    the skinny kernel (tq2_gemm and tq2_gemm_precise), M = 40 the precise
+    tile kernel (the binary16 path cannot hold 1e16)."""
+    c = G.random_case(9050 + m, m, 140, 12416, residual=True)
+    x = c["x"].copy()
+    x[:, :4096] *= np.float32(1e16)
+    x[:, 4096:8192] *= np.float32(1e-16)
+    c["x"] = x
+    c["residual"] = (c["residual"] * np.float32(1e16)).astype(np.float32)
+    c["name"] = "split_falling_rising_m%d" % m
+    if m <= 16:
+        assert_case(tq2, c)
+    assert_case(tq2, c, precise=True)
+
+
+def test_gemm_m1536_k16384_sampled(tq2):
+    """M = 1536, K = 16384 -> N = 3072 (an FFN down-projection shape, K above
+    the 12288 of the 100-layer chain) on the M > 128 kernel: every row of 64
+    sampled output columns, plus the in-place residual on the same columns."""
+    m, n, k = 1536, 3072, 16384
+    rng = np.random.default_rng(9600)
+    aos = G.make_weight(rng, n, k)
+    x = G.make_activations(rng, m, k, outlier_frac=0.01)
+    res = rng.standard_normal((m, n), dtype=np.float32)
+    soa = upload_weight(tq2, aos, n, k)
+    cols = np.sort(rng.choice(n, size=64, replace=False))
+    idx = torch.from_numpy(cols).cuda()
+    xd = _dev(x)
+    for with_res in (False, True):
+        print("m1536 k16384 residual=%s" % with_res, flush=True)
+        out = _dev(res) if with_res else None
+        y = tq2.gemm(soa, xd, n, k, residual=out, out=out)
+        torch.cuda.synchronize()
+        got = y[:, idx].cpu().numpy()
+        ref, s = oracle.matmul_rows(aos, x, n, k, cols, residual=res if with_res else None)
+        ok, msg = check(got, ref, s, tq2.gemm_path(m, n, k), "m1536_k16384 res=%s" % with_res)
+        print(msg, flush=True)
+        assert ok, msg
 
 
 @pytest.mark.parametrize("m", [1, 2, 17])

@@ -174,7 +174,8 @@ def test_q1_special_bits_and_scales(tq2, m):
 
 
 SWIGLU_Q1 = [(1, 300, 4096), (1, 77, 12288), (1, 63, 384), (1, 5, 256), (9, 100, 384),
-             (5, 4100, 4224), (40, 130, 640), (200, 97, 768), (129, 191, 1024)]
+             (5, 4100, 4224), (40, 130, 640), (200, 97, 768), (129, 191, 1024),
+             (150, 50, 12416)]
 
 
 @pytest.mark.parametrize("m,n,k", SWIGLU_Q1)
