@@ -20,8 +20,11 @@
 //    Each weight is decoded once per block and never touches LDS.
 //  * LIMBS = 2 (small M) splits x = hi + lo into two binary16 parts that hit
 //    the same exact weight operand: f32-class accuracy (about 2^-22).
-//  * gemm_pp_kernel (large M) runs its two wave groups half a chunk apart:
+//  * gemm_pp_kernel (M > 128) runs its two wave groups half a chunk apart:
 //    one group issues MFMAs while the other decodes, converts and loads.
+//  * gemm_sp_kernel (16 < M <= 128) splits the waves by role instead: x
+//    waves only stream and convert x, MFMA waves only decode and multiply.
+//  * gemm_kernel serves tq2_gemm_precise beyond M = 16 (x = hi + lo).
 //  * SWIGLU (the ternary counterpart of `fused_gate_up_swiglu_gemm_q1` in the
 //    same table): half of the block's waves take gate-weight columns and the
 //    other half the same columns of the up weight, on the same x tile; the
@@ -564,6 +567,352 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Warp-specialised variant for 16 < M <= 128 (path 2).  4 + XW waves in two
+// roles (a block's wave w runs on SIMD w % 4):
+//  * waves 0..3, the MFMA waves, one per SIMD: with WR = 2 they split the
+//    MT x (2 NW) block tile into four MT/2 x NW quarters (WR = 1: four
+//    MT x NW column slices); each owns all eight MFMA steps of every
+//    256-wide chunk, loads and decodes its weights (two chunks ahead) and
+//    issues the MFMAs, reading x fragments from LDS;
+//  * waves 4 .. 3 + XW, the x waves, only stream x: rows of f32 from global
+//    memory (two chunks in registers), converted to binary16 (RNE) into the
+//    double-buffered LDS tile.
+// x is the largest operand (4 bytes per element, read by every block of an
+// M row block), and each CU's texture unit takes its loads at a fixed rate;
+// when the waves that issue MFMAs also issue those loads, in-order issue
+// holds the MFMAs back behind them.  Split by role, the x waves wait on the
+// texture unit and the MFMA waves on nothing but their own operands.  One
+// barrier per chunk: in iteration c the MFMA waves compute chunk c from
+// buffer c % 2 while the x waves store chunk c + 1 into the other buffer
+// (loaded during iteration c - 1) and issue the loads of chunk c + 2.
+//
+// The 2 x 2 split halves the LDS fragment reads of the M <= 128 tiles (each
+// MFMA wave reads half of the x rows) for twice the weight decode per block,
+// which these short tiles can afford (measured, same process: M = 100,
+// N = 11008, K = 4096 29.6 us against 32.9 us for the 16-column-wave tile
+// kernel; four 1 x 4 MFMA waves with four x waves took 37.4 us).
+//
+// SWIGLU: the MFMA waves of the first half of the column slots read
+// gate-weight columns, the others the same columns of the up weight; the
+// output tile is MT x (NT / 2).  Scales: as in gemm_pp_kernel (LDS_SCALES:
+// preloaded for the whole K, else per chunk).
+template <int MT, int NW, int WR, int XW, bool SWIGLU, Fmt F, bool LDS_SCALES>
+__global__ __launch_bounds__(64 * (4 + XW)) void gemm_sp_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
+    const float* __restrict__ x, const float* __restrict__ residual, float* __restrict__ out,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+  constexpr int CS = 4 / WR;             // column slots of MFMA waves
+  constexpr int MR = MT / WR;            // rows per MFMA wave
+  constexpr int RT = MR / 16;            // 16-row MFMA tiles per MFMA wave
+  constexpr int CG = NW / 16;            // 16-column groups per MFMA wave
+  constexpr int NT = CS * NW;            // weight rows per block
+  constexpr int NO = SWIGLU ? NT / 2 : NT;   // output columns per block
+  constexpr int BITS = int(F);           // code bits per weight
+  constexpr int QW = 2 * BITS;           // code dwords per lane per chunk
+  constexpr int THREADS = 64 * (4 + XW);
+  constexpr int XR = MT / XW;            // x rows per x wave per chunk (one 1 KB load each)
+  static_assert(MT % XW == 0, "x rows per x wave");
+  static_assert(MR % 16 == 0 && NW % 16 == 0 && (WR == 1 || WR == 2), "tile shape");
+  static_assert(!SWIGLU || CS % 2 == 0, "gate/up column slots");
+
+  __shared__ _Float16 As[2][MT][kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[LDS_SCALES ? NT * kPpMaxKB : 8];
+
+  const int ntiles = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  const int mt = t / tiles_n;
+  const int nt = t - mt * tiles_n;
+  const int m0 = mt * MT;
+  const int n0 = nt * NO;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const bool xwave = __builtin_amdgcn_readfirstlane(wave) >= 4;
+  const int wn = wave & 3;                // MFMA waves: wave slot
+  const int xw = wave - 4;                // x waves: row phase (rows xw + XW i)
+  const int rh = wn % WR;                 // MFMA waves: row share (rows rh * MR ..)
+  const int cs = wn / WR;                 // MFMA waves: column slot
+  const bool upw = SWIGLU && __builtin_amdgcn_readfirstlane(cs) >= CS / 2;
+  const int wc = SWIGLU ? cs % (CS / 2) : cs;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int KB = K >> 7;
+  const int nchunks = (K + kChunk - 1) / kChunk;
+  const int mrows = min(MT, M - m0);      // x rows of this block that exist
+
+  // ---- x waves: row wn + 4i of the block, float4 `lane` of the chunk row.
+  // Two register sets, so that a chunk's loads are issued before the previous
+  // chunk's data is waited for.  Rows past M read zeros (buffer range check);
+  // every pass issues the same loads, so the compiler's wait counts stay exact.
+  const rsrc_t rx = make_rsrc(x + size_t(m0) * K, uint32_t(mrows) * uint32_t(K) * 4u);
+  const uint32_t xoff = uint32_t(xw) * uint32_t(K) * 4u + 16u * uint32_t(lane);
+  typedef float4 xregs_t[XR];
+  auto load_x = [&](int c, xregs_t& xr) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i)
+      xr[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rx, xoff + uint32_t(i * XW * K * 4 + c * kChunk * 4), 0, 0));
+  };
+  auto store_x = [&](int buf, const xregs_t& xr) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      const float4 v = xr[i];
+      const half4_t h = {_Float16(v.x), _Float16(v.y), _Float16(v.z), _Float16(v.w)};
+      *reinterpret_cast<half4_t*>(&As[buf][xw + XW * i][4 * lane]) = h;
+    }
+  };
+
+  // ---- MFMA waves: weights of column n0 + wc*NW + 16j + col, k-group g.
+  typedef uint32_t codes_t[QW];
+  const uint32_t row_bytes = uint32_t(K / 8) * uint32_t(BITS);
+  const rsrc_t rc = make_rsrc(upw ? ucodes : codes, uint32_t(N) * row_bytes);
+  const rsrc_t rs = make_rsrc(upw ? uscales : scales, uint32_t(N) * uint32_t(KB) * 2u);
+  const uint32_t nl = uint32_t(n0 + wc * NW + col);
+  const uint32_t code_voff = nl * row_bytes + 8u * BITS * uint32_t(g);
+  const uint32_t scale_voff = (nl * uint32_t(KB) + uint32_t(g >> 1)) * 2u;
+  auto load_w = [&](int c, codes_t (&cw)[CG], uint32_t (&dsc)[CG]) {
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const uint32_t off = code_voff + uint32_t(j * 16) * row_bytes + uint32_t(c * 32 * BITS);
+      if constexpr (QW == 4) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+        cw[j][0] = v[0]; cw[j][1] = v[1]; cw[j][2] = v[2]; cw[j][3] = v[3];
+      } else {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
+        cw[j][0] = v[0]; cw[j][1] = v[1];
+      }
+      if constexpr (!LDS_SCALES)
+        dsc[j] = __builtin_amdgcn_raw_buffer_load_b16(
+            rs, scale_voff + uint32_t(j * 16 * KB * 2 + c * 4), 0, 0);
+    }
+  };
+  // LDS_SCALES: scale of column group j and chunk c (block 2c + (g >> 1));
+  // the chunk is clamped for the passes past the end, and an odd block
+  // count's last second block reads the next row's first scale, which the
+  // caller zeroes.
+  const int ls_base = (cs * NW + col) * KB + (g >> 1);
+  auto scale_bits = [&](int j, int c, const uint32_t (&dsc)[CG]) -> uint32_t {
+    if constexpr (LDS_SCALES) return Ls[ls_base + j * 16 * KB + 2 * min(c, nchunks - 1)];
+    return dsc[j];
+  };
+
+  // Set only by the MFMA waves (in their own loop), so that the x waves'
+  // registers are not held for it during theirs.
+  floatx4_t acc[RT][CG];
+
+  const uint32_t magic = 0x64006400u;
+  auto load_afrags = [&](int buf, int s, half8_t (&a)[RT]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      a[i] = *reinterpret_cast<const half8_t*>(&As[buf][rh * MR + i * 16 + col][64 * g + 8 * s]);
+  };
+  auto decode_bfrags = [&](int s, const codes_t (&cw)[CG], const half2_t (&d2)[CG],
+                           half8_t (&b)[CG]) {
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      if constexpr (F == Fmt::kQ1) {
+        b[j] = decode_step_q1(cw[j][s >> 2], 4 * (s & 3), __builtin_bit_cast(uint32_t, d2[j]));
+      } else {
+        uint32_t w = cw[j][s >> 1];
+        if (s & 1) w >>= 8;
+        b[j] = decode_step(w, d2[j], magic);
+      }
+    }
+  };
+  auto mfmas = [&](const half8_t (&a)[RT], const half8_t (&b)[CG]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CG; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+  // Per step about VALU/MFMA decode instructions and an LDS read every few
+  // MFMAs, instead of long runs of either.
+  constexpr int NMFMA = RT * CG;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < NMFMA; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+      if (q % ((NMFMA + RT - 1) / RT) == 0)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);          // up to three VALU
+    }
+  };
+  auto compute = [&](int c, int buf, const codes_t (&cw_raw)[CG], const uint32_t (&dsc)[CG]) {
+    // binary16 pair (d, d), or (0, 0) where k runs past K in the last chunk
+    // (Q1: the |d| pair, and the words folded by the sign of d).
+    const bool live = c * kChunk + 64 * g < K;
+    half2_t dw[CG];
+    codes_t cw[CG];
+#pragma unroll
+    for (int j = 0; j < CG; ++j) {
+      const uint32_t db = live ? scale_bits(j, c, dsc) & 0xFFFFu : 0u;
+      if constexpr (F == Fmt::kQ1) {
+        dw[j] = __builtin_bit_cast(half2_t, q1_dabs2(db));
+        const uint32_t fold = q1_fold(db);
+#pragma unroll
+        for (int q = 0; q < QW; ++q) cw[j][q] = cw_raw[j][q] ^ fold;
+      } else {
+        const _Float16 d = __builtin_bit_cast(_Float16, uint16_t(db));
+        dw[j] = half2_t{d, d};
+#pragma unroll
+        for (int q = 0; q < QW; ++q) cw[j][q] = cw_raw[j][q];
+      }
+    }
+    half8_t a0[RT], a1[RT], b0[CG], b1[CG];
+    load_afrags(buf, 0, a0);
+    decode_bfrags(0, cw, dw, b0);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if ((s & 1) == 0) {
+        if (s + 1 < 8) {
+          load_afrags(buf, s + 1, a1);
+          decode_bfrags(s + 1, cw, dw, b1);
+        }
+        mfmas(a0, b0);
+      } else {
+        if (s + 1 < 8) {
+          load_afrags(buf, s + 1, a0);
+          decode_bfrags(s + 1, cw, dw, b0);
+        }
+        mfmas(a1, b1);
+      }
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- prologue: (LDS_SCALES) the block's scales into LDS, x chunk 0 in
+  // buffer 0 and chunk 1 in flight, weight chunks 0 and 1 in flight.
+  if constexpr (LDS_SCALES) {
+    auto preload = [&](const uint8_t* plane, int rows, int dst) {
+      const uint32_t valid = uint32_t(min(rows, N - n0)) * uint32_t(KB) * 2u;
+      const uint32_t full = valid & ~15u;
+      const rsrc_t rsb = make_rsrc(plane + size_t(n0) * KB * 2, valid);
+      uint8_t* ls = reinterpret_cast<uint8_t*>(Ls + dst);
+      for (uint32_t o = 16u * uint32_t(tid); o < full; o += 16u * THREADS) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsb, o, 0, 0);
+        *reinterpret_cast<u32x4_t*>(ls + o) = v;
+      }
+      const uint32_t o2 = full + 2u * uint32_t(tid);
+      if (o2 < valid)
+        *reinterpret_cast<uint16_t*>(ls + o2) = __builtin_amdgcn_raw_buffer_load_b16(rsb, o2, 0, 0);
+    };
+    if constexpr (SWIGLU) {
+      preload(scales, NO, 0);
+      preload(uscales, NO, NO * KB);
+    } else {
+      preload(scales, NT, 0);
+    }
+  }
+  // ---- main loops: each role runs its own, with the same number of passes
+  // and barriers (a pass past the last chunk only issues loads); the values
+  // each loop keeps live are then not held by the other role's waves.
+  if (xwave) {
+    // x chunk q lives in set q % 2: pass c stores chunk c + 1 and reloads its
+    // set with chunk c + 3.
+    xregs_t xa, xb;
+    load_x(0, xa);
+    load_x(1, xb);
+    store_x(0, xa);
+    load_x(2, xa);
+    lds_barrier();
+    for (int c = 0; c < nchunks; c += 2) {
+      if (c + 1 < nchunks) store_x(1, xb);
+      load_x(c + 3, xb);
+      lds_barrier();
+      if (c + 2 < nchunks) store_x(0, xa);
+      load_x(c + 4, xa);
+      lds_barrier();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CG; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    codes_t cw0[CG], cw1[CG];
+    uint32_t dr0[CG], dr1[CG];
+    load_w(0, cw0, dr0);
+    load_w(1, cw1, dr1);
+    lds_barrier();
+    auto pass = [&](int c, codes_t (&cw)[CG], uint32_t (&dsc)[CG]) {
+      if (c < nchunks) compute(c, c & 1, cw, dsc);
+      load_w(c + 2, cw, dsc);
+      lds_barrier();
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+      pass(c, cw0, dr0);
+      pass(c + 1, cw1, dr1);
+    }
+  }
+
+  // ---- epilogue --------------------------------------------------------------
+  // (SWIGLU: the up waves hand their sums to the gate waves.)  The finished
+  // MT x NO tile is laid out row-major in LDS and all 512 threads store it in
+  // whole rows, 16 bytes per lane, reading the residual the same way.
+  float* red = reinterpret_cast<float*>(&As[0][0][0]);
+  if constexpr (SWIGLU) {
+    static_assert(2 * RT * CG * 4 * 64 * 4 <= sizeof(As), "reduction buffer");
+    const int slot = rh * (CS / 2) + wc;
+    if (!xwave && upw) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            red[(((slot * RT + i) * CG + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if (!xwave && !upw) {
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[i][j][e] = silu(acc[i][j][e]) * red[(((slot * RT + i) * CG + j) * 4 + e) * 64 + lane];
+    }
+  }
+  // D[n = 4g + e][m = col] of each 16 x 16 result goes to tile row
+  // i * 16 + col, columns wc * NW + j * 16 + 4g .. + 3.
+  constexpr int TP = NO + 4;
+  static_assert(MT * TP * 4 <= sizeof(As), "output tile");
+  float* tile = red;
+  __syncthreads();
+  if (!xwave && !upw) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CG; ++j)
+        *reinterpret_cast<float4*>(&tile[(rh * MR + i * 16 + col) * TP + wc * NW + j * 16 + 4 * g]) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+  }
+  __syncthreads();
+  store_tile<MT, NO, THREADS>(tile, tid, m0, n0, M, N, residual, out);
+}
+
+template <int MT, int NW, int WR, int XW, bool SWIGLU, Fmt F, bool LDS_SCALES>
+hipError_t launch_sp(const uint8_t* soa, const uint8_t* up, const float* x,
+                     const float* residual, float* out, int64_t m, int64_t n, int64_t k,
+                     hipStream_t stream) {
+  constexpr int NO = (SWIGLU ? 2 : 4) / WR * NW;
+  const int64_t tm = (m + MT - 1) / MT;
+  const int64_t tn = (n + NO - 1) / NO;
+  if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(unsigned(tm * tn));
+  const size_t so = scales_offset(F, n, k);
+  hipLaunchKernelGGL((gemm_sp_kernel<MT, NW, WR, XW, SWIGLU, F, LDS_SCALES>), grid,
+                     dim3(64 * (4 + XW)), 0, stream,
+                     soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m), int(n),
+                     int(k), int(tm), int(tn));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Skinny variant for M <= 16 with x split into two binary16 limbs (the
 // f32-class path).  At this M the work per weight is tiny, so the kernel is
 // laid out for the weight stream rather than for matrix-core reuse: the
@@ -878,7 +1227,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(
   constexpr int BITS = int(F);           // code bits per weight
   constexpr int QW = BITS;               // code dwords per lane per chunk
   constexpr int AV = MT * (kChunk / 4) / 2 / GT;   // float4 of x per thread per chunk
-  static_assert(MT % 32 == 0 && NW % 16 == 0, "tile shape");
+  static_assert(MT % 16 == 0 && NW % 16 == 0, "tile shape");
   static_assert((MT / 2) * (kChunk / 4) % GT == 0, "x staging split");
 
   __shared__ _Float16 As[2][MT][kLdsRow];
@@ -1346,16 +1695,22 @@ hipError_t dispatch(int path, const uint8_t* soa, const uint8_t* up, const float
     return launch_tile<64, 16, 4, 2, 2, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
   }
   if (m <= 128) {
-    // One row block of the smallest 16-row multiple that covers M: rows past
-    // M still cost x loads and MFMAs (M = 100: 112 rows, 9% faster than 128).
-    switch ((m + 15) / 16) {
-      case 2: return launch_tile<32, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-      case 3: return launch_tile<48, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-      case 4: return launch_tile<64, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-      case 5: return launch_tile<80, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-      case 6: return launch_tile<96, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-      case 7: return launch_tile<112, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
-      default: return launch_tile<128, 16, 4, 2, 1, SWIGLU, F>(soa, up, x, residual, out, m, n, k, stream);
+    // One row block of the smallest 32-row multiple that covers M, on the
+    // warp-specialised kernel: x rows past M read zeros and their output
+    // rows are not stored.
+    if (k <= int64_t(kPpMaxKB) * kBlockWeights) {
+      switch ((m + 31) / 32) {
+        case 1: return launch_sp<32, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
+        case 2: return launch_sp<64, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
+        case 3: return launch_sp<96, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
+        default: return launch_sp<128, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
+      }
+    }
+    switch ((m + 31) / 32) {
+      case 1: return launch_sp<32, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
+      case 2: return launch_sp<64, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
+      case 3: return launch_sp<96, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
+      default: return launch_sp<128, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
     }
   }
   if (k <= int64_t(kPpMaxKB) * kBlockWeights)

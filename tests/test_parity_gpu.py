@@ -182,7 +182,7 @@ GEMM_SHAPES = [(2, 17, 128), (3, 100, 384), (8, 64, 256), (15, 65, 640), (16, 25
                (17, 200, 384), (31, 33, 128), (32, 300, 512), (33, 100, 256), (64, 129, 384),
                (65, 64, 1024), (96, 192, 256), (97, 250, 640), (128, 300, 512),
                (129, 191, 384), (200, 385, 768), (300, 1000, 1152), (150, 50, 12416),
-               (257, 200, 16512)]
+               (257, 200, 16512), (100, 90, 12416), (33, 70, 16640)]
 
 
 @pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
@@ -589,12 +589,12 @@ def test_swiglu_decode_shapes(tq2, n, k):
     assert_swiglu(tq2, G.swiglu_case(4000 + n + k, 1, n, k))
 
 
-# M = 2..16: split-binary16 kernel; 17..128: 16-column-group kernels; > 128
-# with K <= 12288: the ping-pong kernel; K > 12288: the wide-tile kernel.
+# M = 2..16: split-binary16 kernel; 17..128: the warp-specialised kernel;
+# > 128: the ping-pong kernel (K > 12288: scales loaded per chunk in both).
 SWIGLU_GEMM_SHAPES = [(2, 17, 128), (9, 100, 384), (16, 257, 1024), (5, 4100, 4224),
                       (12, 8200, 2176), (17, 33, 256),
                       (40, 130, 640), (64, 96, 384), (100, 191, 1024), (129, 191, 384),
-                      (200, 97, 768), (300, 1000, 1152), (150, 50, 12416)]
+                      (200, 97, 768), (300, 1000, 1152), (150, 50, 12416), (100, 70, 12416)]
 
 
 @pytest.mark.parametrize("m,n,k", SWIGLU_GEMM_SHAPES)
@@ -602,15 +602,16 @@ def test_swiglu_gemm_shapes(tq2, m, n, k):
     assert_swiglu(tq2, G.swiglu_case(5000 + m + n + k, m, n, k))
 
 
-# Path 2 at 16 < M <= 128 runs one row block of the smallest 16-row multiple
+# Path 2 at 16 < M <= 128 runs one row block of the smallest 32-row multiple
 # covering M (32 ... 128 rows): every tile height, at and just past its edge.
-@pytest.mark.parametrize("m", [40, 48, 49, 70, 80, 81, 90, 96, 105, 112, 113])
+@pytest.mark.parametrize("m", [17, 31, 32, 33, 40, 48, 49, 63, 64, 65, 81, 96, 97, 100, 113,
+                               127, 128])
 def test_tile_heights(tq2, m):
     c = G.random_case(9200 + m, m, 150, 640, residual=(m % 2 == 0))
     assert_case(tq2, c)
 
 
-@pytest.mark.parametrize("m", [49, 81, 105])
+@pytest.mark.parametrize("m", [17, 33, 49, 81, 105, 128])
 def test_swiglu_tile_heights(tq2, m):
     assert_swiglu(tq2, G.swiglu_case(9300 + m, m, 70, 384))
 

@@ -141,7 +141,7 @@ def test_q1_split_path_passes_with_different_scales(tq2):
 Q1_GEMM_SHAPES = [(2, 17, 128), (9, 100, 384), (16, 257, 1024), (5, 4100, 4224), (12, 8200, 2176),
                   (17, 200, 384), (33, 100, 256),
                   (64, 129, 384), (100, 300, 1024), (128, 64, 256), (129, 191, 384),
-                  (200, 385, 768), (300, 1000, 1152), (150, 50, 12416)]
+                  (200, 385, 768), (300, 1000, 1152), (150, 50, 12416), (64, 50, 12416)]
 
 
 @pytest.mark.parametrize("m,n,k", Q1_GEMM_SHAPES)
