@@ -1002,15 +1002,26 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- weights: tile t's code words and scales, PF tiles in flight -------
+    // The MFMA wants lane (col, g) to hold column col's codes for k-group g,
+    // so a quarter-wave (fixed g) would touch 16 weight rows, 16 bytes each:
+    // 64 cache-line accesses per load, about seven times the texture-unit
+    // time of a contiguous 1 KB load.  So the loads use another lane order --
+    // quarter-wave qq reads rows 4qq .. 4qq+3 in full (4 rows x 64 bytes) --
+    // and the words are moved to the MFMA order with a lane permute when the
+    // tile is computed (ds_bpermute: lane (col, g) takes the load lane of
+    // row col, piece g).  The scales follow the same load order.
+    const int lrow = 4 * (lane >> 4) + ((lane >> 2) & 3);
+    const int lpiece = lane & 3;
+    const int perm_addr = 4 * (16 * (col >> 2) + 4 * (col & 3) + g);
     codes_t cw[PF][NMAT][CPW];
-    _Float16 dr[PF][NMAT][CPW];
-    auto load_tile = [&](int t, codes_t (&c)[NMAT][CPW], _Float16 (&d)[NMAT][CPW]) {
-      const uint32_t n = uint32_t(16 * (tile0 + min(t, ntile - 1)) + col);
+    uint32_t dr[PF][NMAT][CPW];
+    auto load_tile = [&](int t, codes_t (&c)[NMAT][CPW], uint32_t (&d)[NMAT][CPW]) {
+      const uint32_t n = uint32_t(16 * (tile0 + min(t, ntile - 1)) + lrow);
 #pragma unroll
       for (int q = 0; q < NMAT; ++q)
 #pragma unroll
         for (int h = 0; h < CPW; ++h) {
-          const uint32_t kk = uint32_t(k0 + 256 * h + 64 * g);
+          const uint32_t kk = uint32_t(k0 + 256 * h + 64 * lpiece);
           const uint32_t off = n * row_bytes + kk / 8u * uint32_t(BITS);
           if constexpr (QW == 4) {
             const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc[q], off, 0, 0);
@@ -1019,9 +1030,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
             const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc[q], off, 0, 0);
             c[q][h][0] = v[0]; c[q][h][1] = v[1];
           }
-          d[q][h] = __builtin_bit_cast(
-              _Float16, __builtin_amdgcn_raw_buffer_load_b16(
-                            rs[q], (n * uint32_t(KB) + (kk >> 7)) * 2u, 0, 0));
+          d[q][h] = __builtin_amdgcn_raw_buffer_load_b16(rs[q], (n * uint32_t(KB) + (kk >> 7)) * 2u,
+                                                         0, 0);
         }
     };
 #pragma unroll
@@ -1089,25 +1099,27 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     }
 
     // ---- stream the tiles ----------------------------------------------------
-    auto compute = [&](int t, const codes_t (&c)[NMAT][CPW], const _Float16 (&d)[NMAT][CPW]) {
+    auto compute = [&](int t, const codes_t (&c)[NMAT][CPW], const uint32_t (&d)[NMAT][CPW]) {
 #pragma unroll
       for (int q = 0; q < NMAT; ++q)
 #pragma unroll
         for (int h = 0; h < CPW; ++h) {
           const bool live = all_live || k0 + 256 * h + 64 * g < K;
-          const _Float16 dd = live ? d[q][h] : _Float16(0.0f);
+          const uint32_t draw = uint32_t(__builtin_amdgcn_ds_bpermute(perm_addr, int(d[q][h])));
+          const uint32_t db = live ? (draw & 0xFFFFu) : 0u;
           uint32_t cf[QW];
+#pragma unroll
+          for (int i = 0; i < QW; ++i)
+            cf[i] = uint32_t(__builtin_amdgcn_ds_bpermute(perm_addr, int(c[q][h][i])));
           half2_t d2;
           if constexpr (F == Fmt::kQ1) {
-            const uint32_t db = __builtin_bit_cast(uint16_t, dd);
             d2 = __builtin_bit_cast(half2_t, q1_dabs2(db));
             const uint32_t fold = q1_fold(db);
 #pragma unroll
-            for (int i = 0; i < QW; ++i) cf[i] = c[q][h][i] ^ fold;
+            for (int i = 0; i < QW; ++i) cf[i] ^= fold;
           } else {
+            const _Float16 dd = __builtin_bit_cast(_Float16, uint16_t(db));
             d2 = half2_t{dd, dd};
-#pragma unroll
-            for (int i = 0; i < QW; ++i) cf[i] = c[q][h][i];
           }
 #pragma unroll
           for (int st = 0; st < 8; ++st) {
