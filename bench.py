@@ -52,6 +52,9 @@ def parse():
                    help="skip the Q1_g128 (1-bit) decode GEMV and M=1536 GEMM lines")
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the decode GEMV size sweep (N = K = 4096, 8192, 16384)")
+    p.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                   help="untimed run-in of the same calls ahead of each timed region (ms of GPU "
+                        "time; a profiler run may shorten it to keep its trace small)")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device-to-device copy of this size (MiB) so a "
                         "counter run can scale FETCH_SIZE / WRITE_SIZE against known bytes")
@@ -206,7 +209,7 @@ def gemv_bytes(n, k, residual):
 # the same calls have run for a while), so each region is preceded by about
 # SETTLE_MS of the same calls, untimed; the region then measures the calls at
 # the clock they settle to.
-SETTLE_MS = 20.0
+SETTLE_MS = 20.0           # --settle-ms
 
 
 def _replay(graphs):
@@ -235,6 +238,8 @@ def time_graphs(torch, graphs, stream, warm=()):
         end.record(stream)
     torch.cuda.synchronize()
     passes = max(1, min(2000, int(math.ceil(SETTLE_MS / max(start.elapsed_time(end), 1e-3)))))
+    if SETTLE_MS <= 0:
+        passes = 0
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
@@ -720,7 +725,9 @@ def q1_bench(torch, tq2, G, dev, stream, args):
 
 
 def main():
+    global SETTLE_MS
     args = parse()
+    SETTLE_MS = args.settle_ms
     if args.gpus != 1:
         print("bench.py: the library runs and is measured on one GPU; --gpus %d is not supported "
               "(run with --gpus 1)" % args.gpus, file=sys.stderr)
