@@ -151,14 +151,16 @@ int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream);
  * same aliasing rules as tq2_gemv.  The kernel is picked by tq2_gemm_path:
  *   0: M == 1, the GEMV above;
  *   1: 2 <= M <= 16: matrix-core GEMM with x split into two binary16 parts
- *      (x = hi + lo), error within 1e-5 * sum|x w| at any magnitude of x:
- *      each wave scales its slice of x (per 4096-wide pass over K) by a power
- *      of two before the split so that both parts stay normal binary16, and
- *      scales the sums back (exact); the power follows the largest |x| the
- *      wave has seen so far (over the rows it holds, in this and earlier
- *      passes), so it only falls and the sums never overflow; an element more
- *      than 2^17 times smaller than that largest |x| keeps an absolute error
- *      below 2^-39 of it;
+ *      (x = hi + lo), error within 1e-5 * sum|x w| at any overall magnitude
+ *      of x: each wave scales its slice of x (per 4096-wide pass over K) by
+ *      a power of two before the split so that both parts stay normal
+ *      binary16, and scales the sums back (exact); the power follows the
+ *      largest |x| the wave has seen so far (over the rows it holds, in this
+ *      and earlier passes), so it only falls and the sums never overflow.
+ *      The bound assumes the elements that carry a row's sum are within
+ *      2^17 of that largest |x|: a smaller element keeps an absolute error
+ *      below 2^-39 of the largest |x|, which can exceed 1e-5 * sum|x w| when
+ *      the largest |x| meets only zero weights;
  *   2: M > 16: matrix-core GEMM with x rounded to binary16 and weights staged
  *      as exact binary16 code * d (oxibonsai-kernels 0.1.5, pipelines.rs,
  *      fields `gemm_tq2_g128_v9_simdgroup` / `gemm_tq2_g128_v10_simdgroup`:
@@ -175,9 +177,10 @@ int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
 /* tq2_gemm with f32-class accuracy at every M: the split-binary16 matrix-core
  * kernel of path 1 (x = hi + lo, both parts against the same exact binary16
  * weight, f32 accumulation) for every M >= 2, and the GEMV for M == 1; error
- * within 1e-5 * sum|x w| at any magnitude of x (for M > 16 the power of two
- * is kept per group of x rows and 256-wide K chunk, falling as larger values
- * arrive, with the sums rescaled to it), at about twice path 2's matrix-core
+ * within 1e-5 * sum|x w| at any overall magnitude of x, under the same
+ * assumption as path 1 (for M > 16 the power of two is kept per group of x
+ * rows and 256-wide K chunk, falling as larger values arrive, with the sums
+ * rescaled to it), at about twice path 2's matrix-core
  * work for M > 16.  The pages stage both operands as binary16 for large M
  * (pipelines.rs, fields `gemm_tq2_g128_v9_simdgroup` /
  * `gemm_tq2_g128_v10_simdgroup`); this is the variant for callers that need
