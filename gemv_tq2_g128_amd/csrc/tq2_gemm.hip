@@ -84,6 +84,25 @@ __device__ __forceinline__ half8_t decode_step(uint32_t word, half2_t d2, uint32
   return b;
 }
 
+// The same four pairs as exact binary16 (c - 1), for a kernel that applies
+// the block scale to the MFMA's result instead.
+__device__ __forceinline__ half8_t decode_step_unit(uint32_t word, uint32_t magic) {
+  half8_t b;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t mask = (3u << (2 * r)) | (3u << (2 * r + 16));
+    const half2_t v = as_half2(and_or(word, mask, magic));
+    const _Float16 sc = _Float16(1.0f / float(1 << (2 * r)));
+    const _Float16 off = _Float16(-(1024.0f / float(1 << (2 * r)) + 1.0f));
+    const half2_t scv = {sc, sc};
+    const half2_t offv = {off, off};
+    const half2_t val = v * scv + offv;
+    b[2 * r] = val[0];
+    b[2 * r + 1] = val[1];
+  }
+  return b;
+}
+
 // Q1: four binary16 pairs (8 weights) of one MFMA step.  Pair p = base + r
 // of `word` has its bits at p and p + 16; shifting left by 15 - p puts them
 // on the two sign bits and the AND-OR adds the magnitude pair `dabs2`
@@ -926,11 +945,21 @@ hipError_t launch_sp(const uint8_t* soa, const uint8_t* up, const float* x,
 // barrier inside the K loop.  The waves' partial sums of each output meet in
 // LDS once, at the end.
 //
-// PACK (M <= 8): the B operand's 16 columns hold the hi limbs of x rows 0..7
+// x is the MFMA's A operand and the weight its B operand, so lane (col, g)
+// accumulates D[m = 4g + e][n = col].  Each MFMA step contracts 32 k's of one
+// 128-weight block: steps 4b .. 4b + 3 of a 256-wide chunk cover its block b,
+// and lane (col, g) holds for block b the two code words (TQ2; one word for
+// Q1) at k = kb + 32 .. of its column, kb = 32 (2 (g & 1) + (g >> 1)) for
+// b = 0 and 128 + 32 (2 (g & 1) + 1 - (g >> 1)) for b = 1; step 4b + s takes
+// k = kb + 8s .. + 7 from both operands.  The weights enter as exact
+// binary16 (c - 1) (Q1: +-1), each block's four steps accumulate into a fresh
+// D, and acc += d * D applies the column's block scale in f32 (one FMA per
+// output and block instead of one packed multiply per weight pair).
+//
+// PACK (M <= 8): the A operand's 16 rows hold the hi limbs of x rows 0..7
 // and the lo limbs of the same rows, so one MFMA per step covers both limbs
-// and output (m, n) is D[n][m] + D[n][m + 8].  Otherwise (M <= 16) the limbs
-// take one MFMA each.  Lane mapping per 256-wide chunk and MFMA step as in
-// gemm_kernel: the fragment of step s is x[col][64g + 8s .. +7].
+// and output (m, n) is D[m][n] + D[m + 8][n].  Otherwise (M <= 16) the limbs
+// take one MFMA each.
 template <int TMAX, int WAVES, bool PACK, bool SWIGLU, Fmt F>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -1007,12 +1036,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     // 64 cache-line accesses per load, about seven times the texture-unit
     // time of a contiguous 1 KB load.  So the loads use another lane order --
     // quarter-wave qq reads rows 4qq .. 4qq+3 in full (4 rows x 64 bytes) --
-    // and the words are moved to the MFMA order with a lane permute when the
-    // tile is computed (ds_bpermute: lane (col, g) takes the load lane of
-    // row col, piece g).  The scales follow the same load order.
+    // and the words are moved to the MFMA order with lane permutes when the
+    // tile is computed.  Load lane (row r, piece p) holds words 4p .. 4p + 3
+    // of the row's chunk (TQ2; Q1: words 2p, 2p + 1) and the scale of block
+    // p >> 1.  Lane (col, g) takes the first half of its registers from piece
+    // g and the second half from piece g ^ 2 of row col: for g < 2 that is
+    // block 0's words, then block 1's; for g >= 2 the other way round, and a
+    // select puts them in block order.  The two scales come from pieces 0
+    // and 2.
     const int lrow = 4 * (lane >> 4) + ((lane >> 2) & 3);
     const int lpiece = lane & 3;
-    const int perm_addr = 4 * (16 * (col >> 2) + 4 * (col & 3) + g);
+    const int perm_row = 4 * (16 * (col >> 2) + 4 * (col & 3));
+    const int perm_a = perm_row + 4 * g;
+    const int perm_b = perm_row + 4 * (g ^ 2);
+    const bool swap_blocks = g >= 2;
+    const int kbase[2] = {32 * (2 * (g & 1) + (g >> 1)), 128 + 32 * (2 * (g & 1) + 1 - (g >> 1))};
     codes_t cw[PF][NMAT][CPW];
     uint32_t dr[PF][NMAT][CPW];
     auto load_tile = [&](int t, codes_t (&c)[NMAT][CPW], uint32_t (&d)[NMAT][CPW]) {
@@ -1057,7 +1095,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     }
     const float mr = wave_max_nonneg(mx);
     const int e = mr > 0.f ? min(e_acc, prescale_exponent(mr)) : e_acc;
-    if (e != e_acc) {                    // wave-uniform; acc only ever scaled down
+    if (pass > 0 && e != e_acc) {        // wave-uniform; acc only ever scaled down (zero in pass 0)
 #pragma unroll
       for (int t = 0; t < TMAX; ++t)
 #pragma unroll
@@ -1095,45 +1133,55 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
       for (int st = 0; st < 8; ++st)
 #pragma unroll
         for (int l = 0; l < LIMBS; ++l)
-          xf[h][st][l] = *reinterpret_cast<const half8_t*>(&xs[(16 * l + col) * kLdsRow + 64 * g + 8 * st]);
+          xf[h][st][l] = *reinterpret_cast<const half8_t*>(
+              &xs[(16 * l + col) * kLdsRow + kbase[st >> 2] + 8 * (st & 3)]);
     }
 
     // ---- stream the tiles ----------------------------------------------------
+    constexpr int BW = QW / 2;               // code words per lane and block
     auto compute = [&](int t, const codes_t (&c)[NMAT][CPW], const uint32_t (&d)[NMAT][CPW]) {
 #pragma unroll
       for (int q = 0; q < NMAT; ++q)
 #pragma unroll
         for (int h = 0; h < CPW; ++h) {
-          const bool live = all_live || k0 + 256 * h + 64 * g < K;
-          const uint32_t draw = uint32_t(__builtin_amdgcn_ds_bpermute(perm_addr, int(d[q][h])));
-          const uint32_t db = live ? (draw & 0xFFFFu) : 0u;
-          uint32_t cf[QW];
+          // Block b of the chunk is past K as a whole or not at all (K is a
+          // multiple of 128); its scale is then taken as 0 (its x is zero).
+          float dv[2];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const bool live = all_live || k0 + 256 * h + 128 * b < K;
+            const uint32_t draw = uint32_t(__builtin_amdgcn_ds_bpermute(perm_row + 8 * b, int(d[q][h])));
+            dv[b] = live ? float(__builtin_bit_cast(_Float16, uint16_t(draw & 0xFFFFu))) : 0.f;
+          }
+          uint32_t raw[QW], cb[2][BW];
 #pragma unroll
           for (int i = 0; i < QW; ++i)
-            cf[i] = uint32_t(__builtin_amdgcn_ds_bpermute(perm_addr, int(c[q][h][i])));
-          half2_t d2;
-          if constexpr (F == Fmt::kQ1) {
-            d2 = __builtin_bit_cast(half2_t, q1_dabs2(db));
-            const uint32_t fold = q1_fold(db);
+            raw[i] = uint32_t(__builtin_amdgcn_ds_bpermute(i < BW ? perm_a : perm_b, int(c[q][h][i])));
 #pragma unroll
-            for (int i = 0; i < QW; ++i) cf[i] ^= fold;
-          } else {
-            const _Float16 dd = __builtin_bit_cast(_Float16, uint16_t(db));
-            d2 = half2_t{dd, dd};
+          for (int i = 0; i < BW; ++i) {
+            cb[0][i] = swap_blocks ? raw[BW + i] : raw[i];
+            cb[1][i] = swap_blocks ? raw[i] : raw[BW + i];
           }
 #pragma unroll
-          for (int st = 0; st < 8; ++st) {
-            half8_t b;
-            if constexpr (F == Fmt::kQ1) {
-              b = decode_step_q1(cf[st >> 2], 4 * (st & 3), __builtin_bit_cast(uint32_t, d2));
-            } else {
-              uint32_t w = cf[st >> 1];
-              if (st & 1) w >>= 8;
-              b = decode_step(w, d2, magic);
+          for (int b = 0; b < 2; ++b) {
+            floatx4_t D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              half8_t w8;
+              if constexpr (F == Fmt::kQ1) {
+                // +-1: the complemented word puts the sign on the weights whose bit is 0.
+                w8 = decode_step_q1(~cb[b][0], 4 * s, 0x3C003C00u);
+              } else {
+                uint32_t w = cb[b][s >> 1];
+                if (s & 1) w >>= 8;
+                w8 = decode_step_unit(w, magic);
+              }
+#pragma unroll
+              for (int l = 0; l < LIMBS; ++l)
+                D = __builtin_amdgcn_mfma_f32_16x16x32_f16(xf[h][4 * b + s][l], w8, D, 0, 0, 0);
             }
 #pragma unroll
-            for (int l = 0; l < LIMBS; ++l)
-              acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, xf[h][st][l], acc[t][q], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) acc[t][q][i] = __builtin_fmaf(dv[b], D[i], acc[t][q][i]);
           }
         }
     };
@@ -1149,8 +1197,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   }
 
   // ---- the waves' partial sums meet in LDS -----------------------------------
-  // acc holds D[n = 4g + e][j = col] of each tile (the weight is the MFMA's
-  // row operand).  red[wave][tile][gate/up][e][lane].
+  // acc holds D[m = 4g + e][n = col] of each tile (x is the MFMA's row
+  // operand).  red[wave][tile][gate/up][e][lane].
   __syncthreads();                       // every wave is done with its x region
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -1173,8 +1221,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const int c = rem & 15;
     const int n = 16 * (tile0 + t) + c;
     if (n >= N) continue;
-    const int ln = m + 16 * (c >> 2);
-    const int e = c & 3;
+    const int ln = c + 16 * (m >> 2);    // PACK: the lo limbs are rows m + 8, lanes ln + 32
+    const int e = m & 3;
     float v[NMAT];
 #pragma unroll
     for (int q = 0; q < NMAT; ++q) {
@@ -1182,7 +1230,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
       for (int w = 0; w < WAVES; ++w) {
         const float* rw = &red[(((w * TMAX + t) * NMAT + q) * 4 + e) * 64];
-        sum += PACK ? rw[ln] + rw[ln + 8] : rw[ln];
+        sum += PACK ? rw[ln] + rw[ln + 32] : rw[ln];
       }
       v[q] = sum;
     }
