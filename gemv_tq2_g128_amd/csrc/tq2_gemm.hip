@@ -147,6 +147,29 @@ __device__ __forceinline__ void split_limbs(float a, float b, uint32_t& hi, uint
   lo = __builtin_bit_cast(uint32_t, l);
 }
 
+// max(m, |a|, |b|) in one instruction.  fmaxf compiles to one extra
+// instruction per input (IEEE-mode canonicalisation); the hardware max
+// itself already returns the other operand for a quiet NaN.
+__device__ __forceinline__ float max3_abs(float m, float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+// Largest value over the wave (v >= 0, not NaN), left in lane 63 and read
+// from there: the same lane moves as wave_max_nonneg, with integer maxima
+// of the bit patterns (which order non-negative floats as the floats).
+__device__ __forceinline__ float wave_max_nonneg_bits(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = max(u, uint32_t(__builtin_amdgcn_update_dpp(0, int(u), 0xB1, 0xF, 0xF, false)));
+  u = max(u, uint32_t(__builtin_amdgcn_update_dpp(0, int(u), 0x4E, 0xF, 0xF, false)));
+  u = max(u, uint32_t(__builtin_amdgcn_update_dpp(0, int(u), 0x141, 0xF, 0xF, false)));
+  u = max(u, uint32_t(__builtin_amdgcn_update_dpp(0, int(u), 0x140, 0xF, 0xF, false)));
+  u = max(u, uint32_t(__builtin_amdgcn_update_dpp(0, int(u), 0x142, 0xA, 0xF, false)));
+  u = max(u, uint32_t(__builtin_amdgcn_update_dpp(0, int(u), 0x143, 0xC, 0xF, false)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(int(u), 63));
+}
+
 // Power-of-two prescale of x for the two-limb (hi + lo) paths: 2^e takes a
 // largest |x| of mx into [2^14, 2^15), so that hi and lo stay clear of
 // binary16's subnormal range whatever the magnitude of x (the scaling is
@@ -960,7 +983,7 @@ hipError_t launch_sp(const uint8_t* soa, const uint8_t* up, const float* x,
 // and the lo limbs of the same rows, so one MFMA per step covers both limbs
 // and output (m, n) is D[m][n] + D[m + 8][n].  Otherwise (M <= 16) the limbs
 // take one MFMA each.
-template <int TMAX, int WAVES, bool PACK, bool SWIGLU, Fmt F>
+template <int TMAX, int WAVES, bool PACK, bool SWIGLU, Fmt F, bool SKIP>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
@@ -1081,6 +1104,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     // 2^e per wave and pass scales x before the split: e is the running
     // exponent, lowered to the prescale_exponent of this slice's largest |x|
     // (over all rows) when that is smaller; acc is brought down to it.
+    // SKIP: rows past M are neither measured nor staged.  Their LDS rows
+    // keep whatever they held, which reaches only rows of D that are not
+    // stored.  The test is a bit mask over the rows past the instance's
+    // smallest M, rather than r < M (which the compiler turns into a variable
+    // trip count, keeping the loop rolled); without SKIP there is no test.
+    const uint32_t xrows = SKIP ? (M >= XR ? ~0u : (1u << M) - 1u) | ((1u << (PACK ? 2 : 9)) - 1u) : ~0u;
     float mx = 0.f;
 #pragma unroll
     for (int h = 0; h < CPW; ++h) {
@@ -1088,12 +1117,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
       float mh = 0.f;
 #pragma unroll
       for (int r = 0; r < XR; ++r) {
-        const float4 v = xq[h][r];
-        mh = fmaxf(fmaxf(mh, fmaxf(fabsf(v.x), fabsf(v.y))), fmaxf(fabsf(v.z), fabsf(v.w)));
+        if ((xrows >> r) & 1u) {         // wave-uniform
+          const float4 v = xq[h][r];
+          mh = max3_abs(mh, v.x, v.y);
+          mh = max3_abs(mh, v.z, v.w);
+        }
       }
-      mx = fmaxf(mx, live ? mh : 0.f);
+      mx = max3_abs(mx, live ? mh : 0.f, 0.f);
     }
-    const float mr = wave_max_nonneg(mx);
+    const float mr = wave_max_nonneg_bits(mx);
     const int e = mr > 0.f ? min(e_acc, prescale_exponent(mr)) : e_acc;
     if (pass > 0 && e != e_acc) {        // wave-uniform; acc only ever scaled down (zero in pass 0)
 #pragma unroll
@@ -1113,8 +1145,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
       if (h > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const bool live = all_live || k0 + 256 * h + 4 * lane < K;
       const uint32_t keep = live ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-      for (int r = 0; r < XR; ++r) {
+      auto stage_row = [&](int r) {
         float4 v = xq[h][r];
         if (!all_live) {                 // wave-uniform
           v.x = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v.x) & keep);
@@ -1127,7 +1158,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         split_limbs(__builtin_amdgcn_ldexpf(v.z, e), __builtin_amdgcn_ldexpf(v.w, e), hi[1], lo[1]);
         *reinterpret_cast<u32x2_t*>(&xs[r * kLdsRow + 4 * lane]) = u32x2_t{hi[0], hi[1]};
         *reinterpret_cast<u32x2_t*>(&xs[(XR + r) * kLdsRow + 4 * lane]) = u32x2_t{lo[0], lo[1]};
-      }
+      };
+#pragma unroll
+      for (int r = 0; r < XR; ++r)
+        if ((xrows >> r) & 1u) stage_row(r);   // wave-uniform
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int st = 0; st < 8; ++st)
@@ -1717,12 +1751,23 @@ hipError_t launch_skinny(const uint8_t* soa, const uint8_t* up, const float* x,
   const dim3 grid(static_cast<unsigned>(blocks));
   // M <= 8 packs both limbs into one MFMA column set and stages 8 x rows per
   // wave, so 16 waves (one 256-wide chunk each) fit the LDS; M <= 16 uses 8.
-  if (m <= 8)
-    hipLaunchKernelGGL((gemm_skinny_kernel<TMAX, 16, true, SWIGLU, F>), grid, dim3(1024), 0,
+  // Where at least a quarter of the staged rows would be padding (M <= 4 of
+  // 8, M <= 12 of 16) the instance skips the rows past M; with fewer, the
+  // per-row tests cost more than the rows they save (measured).
+  if (m <= 4)
+    hipLaunchKernelGGL((gemm_skinny_kernel<TMAX, 16, true, SWIGLU, F, true>), grid, dim3(1024), 0,
+                       stream, soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m),
+                       int(n), int(k));
+  else if (m <= 8)
+    hipLaunchKernelGGL((gemm_skinny_kernel<TMAX, 16, true, SWIGLU, F, false>), grid, dim3(1024), 0,
+                       stream, soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m),
+                       int(n), int(k));
+  else if (m <= 12)
+    hipLaunchKernelGGL((gemm_skinny_kernel<TMAX, 8, false, SWIGLU, F, true>), grid, dim3(512), 0,
                        stream, soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m),
                        int(n), int(k));
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<TMAX, 8, false, SWIGLU, F>), grid, dim3(512), 0,
+    hipLaunchKernelGGL((gemm_skinny_kernel<TMAX, 8, false, SWIGLU, F, false>), grid, dim3(512), 0,
                        stream, soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m),
                        int(n), int(k));
   return hipGetLastError();
