@@ -321,10 +321,10 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
       for (int i = 0; i < AV; ++i) {
         const int c4 = (tid + THREADS * i) & 63;
         if (c * kChunk + 4 * c4 >= K) va[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        mh = fmaxf(fmaxf(mh, fmaxf(fabsf(va[i].x), fabsf(va[i].y))),
-                   fmaxf(fabsf(va[i].z), fabsf(va[i].w)));
+        mh = max3_abs(mh, va[i].x, va[i].y);
+        mh = max3_abs(mh, va[i].z, va[i].w);
       }
-      const float mr = wave_max_nonneg(mh);
+      const float mr = wave_max_nonneg_bits(mh);
       if (mr > 0.f) erun = min(erun, prescale_exponent(mr));   // a zero chunk says nothing
       if (lane == 0) xexp[buf][wave] = erun;
 #pragma unroll
@@ -341,12 +341,15 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
       const int r = f >> 6;
       const int c4 = f & 63;
       const float4 v = va[i];
-      half4_t h = {_Float16(v.x), _Float16(v.y), _Float16(v.z), _Float16(v.w)};
-      *reinterpret_cast<half4_t*>(&As[buf][0][r][4 * c4]) = h;
       if constexpr (LIMBS == 2) {
-        half4_t l = {_Float16(v.x - float(h[0])), _Float16(v.y - float(h[1])),
-                     _Float16(v.z - float(h[2])), _Float16(v.w - float(h[3]))};
-        *reinterpret_cast<half4_t*>(&As[buf][LIMBS - 1][r][4 * c4]) = l;
+        uint32_t hi[2], lo[2];
+        split_limbs(v.x, v.y, hi[0], lo[0]);
+        split_limbs(v.z, v.w, hi[1], lo[1]);
+        *reinterpret_cast<u32x2_t*>(&As[buf][0][r][4 * c4]) = u32x2_t{hi[0], hi[1]};
+        *reinterpret_cast<u32x2_t*>(&As[buf][1][r][4 * c4]) = u32x2_t{lo[0], lo[1]};
+      } else {
+        const half4_t h = {_Float16(v.x), _Float16(v.y), _Float16(v.z), _Float16(v.w)};
+        *reinterpret_cast<half4_t*>(&As[buf][0][r][4 * c4]) = h;
       }
     }
   };
