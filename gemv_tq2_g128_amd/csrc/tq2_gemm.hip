@@ -975,9 +975,9 @@ hipError_t launch_sp(const uint8_t* soa, const uint8_t* up, const float* x,
 // accumulates D[m = 4g + e][n = col].  Each MFMA step contracts 32 k's of one
 // 128-weight block: steps 4b .. 4b + 3 of a 256-wide chunk cover its block b,
 // and lane (col, g) holds for block b the two code words (TQ2; one word for
-// Q1) at k = kb + 32 .. of its column, kb = 32 (2 (g & 1) + (g >> 1)) for
-// b = 0 and 128 + 32 (2 (g & 1) + 1 - (g >> 1)) for b = 1; step 4b + s takes
-// k = kb + 8s .. + 7 from both operands.  The weights enter as exact
+// Q1) of its column that cover k = kb .. kb + 31, with kb = 32 (2 (g & 1) +
+// (g >> 1)) for b = 0 and 128 + 32 (2 (g & 1) + 1 - (g >> 1)) for b = 1;
+// step 4b + s takes k = kb + 8s .. + 7 from both operands.  The weights enter as exact
 // binary16 (c - 1) (Q1: +-1), each block's four steps accumulate into a fresh
 // D, and acc += d * D applies the column's block scale in f32 (one FMA per
 // output and block instead of one packed multiply per weight pair).
