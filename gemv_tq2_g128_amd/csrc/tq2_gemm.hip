@@ -620,11 +620,12 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
 //    256-wide chunk, loads and decodes its weights (two chunks ahead) and
 //    issues the MFMAs, reading x fragments from LDS;
 //  * waves 4 .. 3 + XW, the x waves, only stream x: each a contiguous run
-//    of MT / XW rows of f32 from global memory (two chunks in registers),
-//    converted to binary16 (RNE) into the double-buffered LDS tile.  A run
-//    that lies wholly past M is not loaded at all (at M = 100 one of the
-//    eight runs of the 128-row tile), which took 27.2 -> 25.3 us at M = 100,
-//    N = 11008, K = 4096 against rows interleaved over the waves.
+//    of XR rows of f32 from global memory (two chunks in registers),
+//    converted to binary16 (RNE) into the double-buffered LDS tile.  XR is
+//    MT / XW, or 13 for the 128-row tile when M <= 104 (104 rows staged).
+//    A run that lies wholly past M is not loaded at all.  Against rows
+//    interleaved over the waves: 27.2 -> 25.3 us at M = 100, N = 11008,
+//    K = 4096, and 24.6 us with XR = 13.
 // x is the largest operand (4 bytes per element, read by every block of an
 // M row block), and each CU's texture unit takes its loads at a fixed rate;
 // when the waves that issue MFMAs also issue those loads, in-order issue
@@ -644,7 +645,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_kernel(
 // gate-weight columns, the others the same columns of the up weight; the
 // output tile is MT x (NT / 2).  Scales: as in gemm_pp_kernel (LDS_SCALES:
 // preloaded for the whole K, else per chunk).
-template <int MT, int NW, int WR, int XW, bool SWIGLU, Fmt F, bool LDS_SCALES>
+template <int MT, int NW, int WR, int XW, bool SWIGLU, Fmt F, bool LDS_SCALES, int XR>
 __global__ __launch_bounds__(64 * (4 + XW)) void gemm_sp_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const uint8_t* __restrict__ ucodes, const uint8_t* __restrict__ uscales,
@@ -659,8 +660,11 @@ __global__ __launch_bounds__(64 * (4 + XW)) void gemm_sp_kernel(
   constexpr int BITS = int(F);           // code bits per weight
   constexpr int QW = 2 * BITS;           // code dwords per lane per chunk
   constexpr int THREADS = 64 * (4 + XW);
-  constexpr int XR = MT / XW;            // x rows per x wave per chunk (one 1 KB load each)
-  static_assert(MT % XW == 0, "x rows per x wave");
+  // XR: x rows per x wave per chunk (one 1 KB load each).  XR * XW may be
+  // smaller than MT when the caller's M fits in XR * XW rows; the tile rows
+  // past XR * XW are then never staged and reach only results that are not
+  // stored.
+  static_assert(XR * XW <= MT && XR * XW > MT - 32, "x rows per x wave");
   static_assert(MR % 16 == 0 && NW % 16 == 0 && (WR == 1 || WR == 2), "tile shape");
   static_assert(!SWIGLU || CS % 2 == 0, "gate/up column slots");
 
@@ -955,7 +959,7 @@ __global__ __launch_bounds__(64 * (4 + XW)) void gemm_sp_kernel(
   store_tile<MT, NO, THREADS>(tile, tid, m0, n0, M, N, residual, out);
 }
 
-template <int MT, int NW, int WR, int XW, bool SWIGLU, Fmt F, bool LDS_SCALES>
+template <int MT, int NW, int WR, int XW, bool SWIGLU, Fmt F, bool LDS_SCALES, int XR = MT / XW>
 hipError_t launch_sp(const uint8_t* soa, const uint8_t* up, const float* x,
                      const float* residual, float* out, int64_t m, int64_t n, int64_t k,
                      hipStream_t stream) {
@@ -965,7 +969,9 @@ hipError_t launch_sp(const uint8_t* soa, const uint8_t* up, const float* x,
   if (tm * tn > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid(unsigned(tm * tn));
   const size_t so = scales_offset(F, n, k);
-  hipLaunchKernelGGL((gemm_sp_kernel<MT, NW, WR, XW, SWIGLU, F, LDS_SCALES>), grid,
+  // Rows the x waves would not stage (only where XR * XW < MT).
+  if (int64_t(XR) * XW < MT && m > int64_t(XR) * XW) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_sp_kernel<MT, NW, WR, XW, SWIGLU, F, LDS_SCALES, XR>), grid,
                      dim3(64 * (4 + XW)), 0, stream,
                      soa, soa + so, up, up ? up + so : nullptr, x, residual, out, int(m), int(n),
                      int(k), int(tm), int(tn));
@@ -1826,14 +1832,21 @@ hipError_t dispatch(int path, const uint8_t* soa, const uint8_t* up, const float
         case 1: return launch_sp<32, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
         case 2: return launch_sp<64, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
         case 3: return launch_sp<96, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
-        default: return launch_sp<128, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
+        default:
+          // Up to M = 104, eight x waves of 13 rows cover M with fewer loads.
+          if (m <= 104)
+            return launch_sp<128, 32, 2, 8, SWIGLU, F, true, 13>(soa, up, x, residual, out, m, n, k, stream);
+          return launch_sp<128, 32, 2, 8, SWIGLU, F, true>(soa, up, x, residual, out, m, n, k, stream);
       }
     }
     switch ((m + 31) / 32) {
       case 1: return launch_sp<32, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
       case 2: return launch_sp<64, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
       case 3: return launch_sp<96, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
-      default: return launch_sp<128, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
+      default:
+        if (m <= 104)
+          return launch_sp<128, 32, 2, 8, SWIGLU, F, false, 13>(soa, up, x, residual, out, m, n, k, stream);
+        return launch_sp<128, 32, 2, 8, SWIGLU, F, false>(soa, up, x, residual, out, m, n, k, stream);
     }
   }
   if (k <= int64_t(kPpMaxKB) * kBlockWeights)

@@ -603,9 +603,10 @@ def test_swiglu_gemm_shapes(tq2, m, n, k):
 
 
 # Path 2 at 16 < M <= 128 runs one row block of the smallest 32-row multiple
-# covering M (32 ... 128 rows): every tile height, at and just past its edge.
-@pytest.mark.parametrize("m", [17, 31, 32, 33, 40, 48, 49, 63, 64, 65, 81, 96, 97, 100, 113,
-                               127, 128])
+# covering M (32 ... 128 rows): every tile height, at and just past its edge,
+# and both sides of M = 104, up to which the 128-row tile stages 104 rows.
+@pytest.mark.parametrize("m", [17, 31, 32, 33, 40, 48, 49, 63, 64, 65, 81, 96, 97, 100, 104,
+                               105, 113, 127, 128])
 def test_tile_heights(tq2, m):
     c = G.random_case(9200 + m, m, 150, 640, residual=(m % 2 == 0))
     assert_case(tq2, c)
