@@ -681,7 +681,10 @@ def small_batch_bench(torch, tq2, G, dev, stream, args):
     d ~ U[0.005, 0.05]) at the workload's M = 7, 8, 9 and 100; the weight is
     rotated over copies larger than the Infinity Cache, as for the GEMV.
     Reported per M: time per call, algorithmic bytes (weight + x + out) per
-    second and the fraction of the HBM peak, and the path taken."""
+    second and the fraction of the HBM peak, and the path taken.  Where
+    tq2_gemm_workspace_bytes is nonzero (M = 100) the line times tq2_gemm_ws
+    with its workspace (entry "tq2_gemm_ws"), and "m100_tq2_gemm" times
+    tq2_gemm itself on the same inputs."""
     import numpy as np
     out_lines = {}
     c = G.config3(100)
@@ -691,14 +694,22 @@ def small_batch_bench(torch, tq2, G, dev, stream, args):
     pool = max(1, int(math.ceil(args.pool_mib * 2 ** 20 / sb)))
     wpool = soa.repeat(pool)
     base = wpool.data_ptr()
-    for m in (7, 8, 9, 100):
+    for key, m, use_ws in (("m7", 7, True), ("m8", 8, True), ("m9", 9, True), ("m100", 100, True),
+                           ("m100_tq2_gemm", 100, False)):
         # config3(m)'s x is the first m rows of the same 100-row draw
         x = torch.from_numpy(np.ascontiguousarray(c["x"][:m])).to(dev)
         out = torch.empty((m, n), dtype=torch.float32, device=dev)
+        need = tq2.gemm_workspace_bytes(m, n, k) if use_ws else 0
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
-        def call(i, x=x, out=out, m=m):
-            st = tq2.gemm_ptr(base + (i % pool) * sb, x.data_ptr(), 0, out.data_ptr(), m, n, k,
-                              torch.cuda.current_stream(dev).cuda_stream)
+        def call(i, x=x, out=out, m=m, ws=ws, need=need):
+            if need:
+                st = tq2.gemm_ws_ptr(base + (i % pool) * sb, x.data_ptr(), 0, out.data_ptr(), m, n,
+                                     k, ws.data_ptr(), need,
+                                     torch.cuda.current_stream(dev).cuda_stream)
+            else:
+                st = tq2.gemm_ptr(base + (i % pool) * sb, x.data_ptr(), 0, out.data_ptr(), m, n, k,
+                                  torch.cuda.current_stream(dev).cuda_stream)
             if st != 0:
                 raise RuntimeError("tq2_gemm failed: %s" % tq2.status_string(st))
 
@@ -709,11 +720,14 @@ def small_batch_bench(torch, tq2, G, dev, stream, args):
         us = ms * 1e3 / (reps * pool)
         nbytes = n * (k // 128) * 34 + 4 * m * k + 4 * m * n
         gbs = nbytes / (us * 1e-6) / 1e9
-        out_lines["m%d" % m] = {"us_per_call": round(us, 3), "gbs": round(gbs, 2),
-                                "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 2),
-                                "path": tq2.gemm_path(m, n, k), "calls": reps * pool}
-        del g
+        tflops = 2.0 * m * n * k / (us * 1e-6) / 1e12
+        out_lines[key] = {"us_per_call": round(us, 3), "gbs": round(gbs, 2),
+                          "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                          "tflops": round(tflops, 2),
+                          "frac_of_f16_peak": round(tflops / F16_MFMA_PEAK_TFLOPS, 4),
+                          "path": tq2.gemm_path(m, n, k), "calls": reps * pool,
+                          "entry": "tq2_gemm_ws" if need else "tq2_gemm"}
+        del g, ws
     del wpool
     return {"gemm_small_batch_k4096_n11008": out_lines}
 

@@ -253,6 +253,34 @@ int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
   return gemm_impl(tq2::Fmt::kTq2, tq2_gemm_path(m, n, k), soa, x, residual, out, m, n, k, stream);
 }
 
+size_t tq2_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (check_shape(m, n, k) != TQ2_OK || m == 0 || n == 0) return 0;
+  if (tq2_gemm_path(m, n, k) != 2 || !gemm_shape_fits(n, k)) return 0;
+  return tq2::gemm_ws_bytes(m, n, k);
+}
+
+int tq2_gemm_ws(const void* soa, const float* x, const float* residual, float* out, int64_t m,
+                int64_t n, int64_t k, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_shape(m, n, k);
+  if (st != TQ2_OK) return st;
+  if (m == 0 || n == 0) return TQ2_OK;
+  const size_t need = tq2_gemm_workspace_bytes(m, n, k);
+  if (need == 0) return tq2_gemm(soa, x, residual, out, m, n, k, stream);
+  st = check_matmul_host(soa, x, residual, out, m, n, k);
+  if (st != TQ2_OK) return st;
+  if (!workspace || workspace_bytes < need) return TQ2_ERR_INVALID;
+  if (!aligned(workspace, 256)) return TQ2_ERR_ALIGN;
+  const size_t ob = size_t(m) * size_t(n) * 4;
+  if (overlaps(workspace, need, x, size_t(m) * size_t(k) * 4) ||
+      overlaps(workspace, need, out, ob) || overlaps(workspace, need, residual, ob) ||
+      overlaps(workspace, need, soa, tq2::soa_bytes(n, k)))
+    return TQ2_ERR_ALIAS;
+  st = check_device();
+  if (st != TQ2_OK) return st;
+  return launch_status(tq2::launch_gemm_ws(static_cast<const uint8_t*>(soa), x, residual, out, m,
+                                           n, k, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int tq2_gemm_precise(const void* soa, const float* x, const float* residual, float* out,
                      int64_t m, int64_t n, int64_t k, void* stream) {
   const int st = check_shape(m, n, k);

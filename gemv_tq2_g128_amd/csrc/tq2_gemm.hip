@@ -979,6 +979,380 @@ hipError_t launch_sp(const uint8_t* soa, const uint8_t* up, const float* x,
 }
 
 // ---------------------------------------------------------------------------
+// K-split variant for 16 < M <= 128 with x converted once per call (path 2,
+// tq2_gemm_ws).  Each CU of gemm_sp_kernel streams all of x in f32 from L2,
+// and a CU takes about 118 GB/s from L2 however the loads are spread over
+// its waves (measured with contiguous 16-byte-per-lane loads): 1.64 MB of x
+// at M = 100, K = 4096 is 14 us per block before any arithmetic.  Reading x
+// in MFMA fragment order straight from its f32 rows is worse still (35 GB/s
+// per CU: a 16-row fragment touches 16 lines one row pitch apart).  So a
+// pre-pass writes x once per call as binary16 fragments into a workspace
+// (half the bytes, each fragment a contiguous 1 KB), and the GEMM's waves
+// load those fragments directly into operand registers: no x tile in LDS,
+// no staging waves and no barrier inside the K loop.
+//
+// x16_fragments_kernel: fragment (rt, c, s), 1 KB, holds for lane
+// l = 16 g + col the binary16 (RNE) values x[16 rt + col][256 c + 64 g +
+// 8 s .. + 7], the B operand of MFMA step s of chunk c for row tile rt in the
+// chunk bookkeeping above.  Rows past M and k past K are written as zeros.
+// One block per (rt, c): thread t reads 16 consecutive k (64 bytes) of row
+// t / 16 (whole 1 KB rows per 16 threads), puts its two 8-value groups in
+// their fragment slots in LDS, and the block then writes its 8 fragments
+// (8 KB, contiguous in the workspace) 32 bytes per thread.
+__global__ __launch_bounds__(256) void x16_fragments_kernel(const float* __restrict__ x, int M,
+                                                            int K, int nch,
+                                                            u32x4_t* __restrict__ frag) {
+  __shared__ u32x4_t sl[8 * 64];
+  const int c = int(blockIdx.x) % nch;
+  const int rt = int(blockIdx.x) / nch;
+  const int t = threadIdx.x;
+  const int r = t >> 4, seg = t & 15;          // row in the tile, 16-wide k segment
+  const int m = 16 * rt + r;
+  const int k0 = c * kChunk + 16 * seg;
+  u32x4_t h0 = {0u, 0u, 0u, 0u}, h1 = {0u, 0u, 0u, 0u};
+  if (m < M && k0 < K) {
+    const float4* p = reinterpret_cast<const float4*>(x + size_t(m) * uint32_t(K) + k0);
+    const float4 a = p[0], b = p[1], e = p[2], f = p[3];
+    auto pk = [](float u, float v) { return __builtin_bit_cast(uint32_t, half2_t{_Float16(u), _Float16(v)}); };
+    h0 = u32x4_t{pk(a.x, a.y), pk(a.z, a.w), pk(b.x, b.y), pk(b.z, b.w)};
+    h1 = u32x4_t{pk(e.x, e.y), pk(e.z, e.w), pk(f.x, f.y), pk(f.z, f.w)};
+  }
+  // k = 64 g + 8 st + i inside the chunk: this thread's groups are
+  // g = seg / 4, st = 2 (seg % 4) and st + 1, for lane 16 g + r.
+  const int g = seg >> 2, st = 2 * (seg & 3);
+  sl[st * 64 + 16 * g + r] = h0;
+  sl[(st + 1) * 64 + 16 * g + r] = h1;
+  __syncthreads();
+  u32x4_t* dst = frag + (size_t(rt) * uint32_t(nch) + uint32_t(c)) * 512u;
+  dst[2 * t] = sl[2 * t];
+  dst[2 * t + 1] = sl[2 * t + 1];
+}
+
+// gemm_ks_kernel: block = all RT * 16 rows (one row block, 16 < M <= 128)
+// x CT * 16 weight columns, 8 waves (two per SIMD).  Wave w owns the chunks
+// [w nch / 8, (w + 1) nch / 8) of K: for each it takes the chunk's code words
+// and scales of its CT column groups and streams the chunk's 8 x RT x
+// fragments through RT x CT MFMAs per step, decoding each weight once for all
+// rows.  Nothing is shared between the waves until their partial sums meet
+// in LDS at the end, in a fixed order (waves w and w + 4, then the four
+// sums), so results are deterministic.  Two waves per SIMD let one wave's
+// decode overlap the other's MFMAs.
+//
+// LDS_W (TQ2, K <= kKsMaxK): the block first copies its whole weight slice
+// (codes in MFMA lane order, and scales) into LDS, so that the K loop's only
+// global loads are the x fragments.  Vector loads complete in issue order: a
+// chunk's code words, fetched from HBM inside the loop, held back every x
+// fragment issued after them (at M = 100, N = 11008, K = 4096 the kernel
+// takes 15.3 us with the staged weights, 16.3 us with per-chunk loads).
+// Otherwise each wave loads its chunks' weights from global memory a chunk
+// ahead.
+constexpr int kKsLdsBytes = 156 * 1024;
+constexpr int64_t kKsMaxK = 12288;           // staged weights: 48 columns x K, plus scales
+
+template <int RT, int CT, int RING, Fmt F, bool LDS_W>
+__global__ __launch_bounds__(512) void gemm_ks_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const u32x4_t* __restrict__ frag, const float* __restrict__ residual,
+    float* __restrict__ out, int M, int N, int K, int nch) {
+  constexpr int NO = 16 * CT;
+  constexpr int BITS = int(F);
+  constexpr int QW = 2 * BITS;                 // code dwords per lane per chunk
+  static_assert(!LDS_W || F == Fmt::kTq2, "staged weights use the TQ2 lane order");
+  static_assert(4 * RT * CT * 64 * 16 <= kKsLdsBytes, "reduction buffer");
+  static_assert(!LDS_W || (kKsMaxK / kChunk) * CT * 1024 + NO * (kKsMaxK / 128) * 2 <= kKsLdsBytes,
+                "staged weights");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kKsLdsBytes];
+
+  const int n0 = blockIdx.x * NO;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int KB = K >> 7;
+  const int c0 = (wave * nch) >> 3;
+  const int c1 = ((wave + 1) * nch) >> 3;
+
+  typedef uint32_t codes_t[QW];
+  const uint32_t row_bytes = uint32_t(K / 8) * uint32_t(BITS);
+  const rsrc_t rx = make_rsrc(frag, uint32_t(RT) * uint32_t(nch) * 8u * 1024u);
+  const uint32_t xrt = uint32_t(nch) * 8u * 1024u;     // bytes per row tile
+  // Fragment loads past the wave's (or the matrix's) last chunk are issued
+  // anyway: they read another wave's data or, past the end, zeros (range
+  // check), and keep every load unconditional.
+  auto load_x = [&](int c, int st, u32x4_t (&xf)[RT]) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      xf[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, uint32_t(i) * xrt + uint32_t((c * 8 + st) * 1024) + 16u * uint32_t(lane), 0, 0);
+  };
+
+  // Staged weights: wl[(c * CT + j) * 64 + lane] holds the four code words
+  // lane (col, g) of column group j uses in chunk c; sl[n * KB + kb] the
+  // scales of the block's columns.
+  const u32x4_t* wl = reinterpret_cast<const u32x4_t*>(smem);
+  const uint16_t* sl = reinterpret_cast<const uint16_t*>(smem + size_t(nch) * CT * 1024);
+  // Global weights (not LDS_W): column n0 + 16 j + col, k-group g.
+  const uint32_t nl = uint32_t(n0 + col);
+  const uint32_t code_voff = nl * row_bytes + 8u * BITS * uint32_t(g);
+  const uint32_t scale_voff = (nl * uint32_t(KB) + uint32_t(g >> 1)) * 2u;
+  const rsrc_t rc = make_rsrc(codes, uint32_t(N) * row_bytes);
+  const rsrc_t rs = make_rsrc(scales, uint32_t(N) * uint32_t(KB) * 2u);
+  auto load_w = [&](int c, codes_t (&cw)[CT], uint32_t (&dsc)[CT]) {
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+      if constexpr (LDS_W) {
+        const u32x4_t v = wl[(c * CT + j) * 64 + lane];
+        cw[j][0] = v[0]; cw[j][1] = v[1]; cw[j][2] = v[2]; cw[j][3] = v[3];
+        dsc[j] = sl[(16 * j + col) * KB + 2 * c + (g >> 1)];
+      } else {
+        const uint32_t off = code_voff + uint32_t(j * 16) * row_bytes + uint32_t(c * 32 * BITS);
+        if constexpr (QW == 4) {
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0);
+          cw[j][0] = v[0]; cw[j][1] = v[1]; cw[j][2] = v[2]; cw[j][3] = v[3];
+        } else {
+          const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rc, off, 0, 0);
+          cw[j][0] = v[0]; cw[j][1] = v[1];
+        }
+        dsc[j] = __builtin_amdgcn_raw_buffer_load_b16(
+            rs, scale_voff + uint32_t(j * 16 * KB * 2 + c * 4), 0, 0);
+      }
+    }
+  };
+
+  // A ring of RING (2 or 4, a divisor of 8) steps' fragments: step st of a
+  // chunk reads slot st % RING and loads step st + RING - 1 into the slot
+  // freed by step st - 1, so each load has RING - 1 steps' work to arrive.
+  // The first RING - 1 steps go out before anything else.  Two slots are
+  // used: with four, the loop was slower (M = 100, N = 11008, K = 4096:
+  // 16.8 - 17.5 against 15.3 us per kernel; RT = 7 then spills).
+  static_assert(RING == 2 || RING == 4, "ring depth");
+  u32x4_t xr[RING][RT];
+  if (c0 < c1) {
+#pragma unroll
+    for (int q = 0; q < RING - 1; ++q) load_x(c0, q, xr[q]);
+  }
+
+  if constexpr (LDS_W) {
+    // The block's weight slice into LDS: 16-byte units u = (column jn, unit
+    // t16 = 4 c + g of its row), 8 loads in flight per thread, columns past
+    // N read as zeros.
+    const int live_cols = min(NO, N - n0);
+    const rsrc_t rcb = make_rsrc(codes + size_t(n0) * row_bytes, uint32_t(live_cols) * row_bytes);
+    const rsrc_t rsb = make_rsrc(scales + size_t(n0) * uint32_t(KB) * 2u,
+                                 uint32_t(live_cols) * uint32_t(KB) * 2u);
+    const int upc = K >> 6;                    // 16-byte units per column row
+    const int units = NO * upc;
+    u32x4_t* wls = reinterpret_cast<u32x4_t*>(smem);
+    for (int base = 0; base < units; base += 8 * 512) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int u = base + q * 512 + tid;
+        const int jn = u / upc, t16 = u - jn * upc;
+        const uint32_t off = u < units ? uint32_t(jn) * row_bytes + 16u * uint32_t(t16) : 0xFFFFFFF0u;
+        v[q] = __builtin_amdgcn_raw_buffer_load_b128(rcb, off, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int u = base + q * 512 + tid;
+        if (u < units) {
+          const int jn = u / upc, t16 = u - jn * upc;
+          wls[((t16 >> 2) * CT + (jn >> 4)) * 64 + 16 * (t16 & 3) + (jn & 15)] = v[q];
+        }
+      }
+    }
+    uint16_t* sls = reinterpret_cast<uint16_t*>(smem + size_t(nch) * CT * 1024);
+    for (int u = tid; u < NO * KB; u += 512)
+      sls[u] = __builtin_amdgcn_raw_buffer_load_b16(rsb, 2u * uint32_t(u), 0, 0);
+    lds_barrier();
+  }
+
+  floatx4_t acc[RT][CT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < CT; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t magic = 0x64006400u;
+  if (c0 < c1) {
+    codes_t cw[CT];
+    uint32_t dsc[CT];
+    load_w(c0, cw, dsc);
+    for (int c = c0; c < c1; ++c) {
+      codes_t cwn[CT];
+      uint32_t dsn[CT];
+      load_w(c + 1, cwn, dsn);
+      __builtin_amdgcn_sched_barrier(0);
+      // binary16 pair (d, d), or (0, 0) where k runs past K in the last
+      // chunk (Q1: the |d| pair, and the words folded by the sign of d).
+      const bool live = c * kChunk + 64 * g < K;
+      half2_t dw[CT];
+      codes_t cwd[CT];
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        const uint32_t db = live ? dsc[j] & 0xFFFFu : 0u;
+        if constexpr (F == Fmt::kQ1) {
+          dw[j] = __builtin_bit_cast(half2_t, q1_dabs2(db));
+          const uint32_t fold = q1_fold(db);
+#pragma unroll
+          for (int q = 0; q < QW; ++q) cwd[j][q] = cw[j][q] ^ fold;
+        } else {
+          const _Float16 d = __builtin_bit_cast(_Float16, uint16_t(db));
+          dw[j] = half2_t{d, d};
+#pragma unroll
+          for (int q = 0; q < QW; ++q) cwd[j][q] = cw[j][q];
+        }
+      }
+      auto step = [&](int st, const u32x4_t (&xc)[RT], u32x4_t (&xn)[RT]) {
+        // Step st + RING - 1's fragments (past step 7: the next chunk's).
+        if (st + RING - 1 < 8)
+          load_x(c, st + RING - 1, xn);
+        else
+          load_x(c + 1, st + RING - 1 - 8, xn);
+        // Keep these loads ahead of the step's arithmetic (the scheduler
+        // would sink them to their registers' last use).
+        __builtin_amdgcn_sched_barrier(0);
+        half8_t b[CT];
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+          if constexpr (F == Fmt::kQ1) {
+            b[j] = decode_step_q1(cwd[j][st >> 2], 4 * (st & 3),
+                                  __builtin_bit_cast(uint32_t, dw[j]));
+          } else {
+            uint32_t w = cwd[j][st >> 1];
+            if (st & 1) w >>= 8;
+            b[j] = decode_step(w, dw[j], magic);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+          for (int j = 0; j < CT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                b[j], __builtin_bit_cast(half8_t, xc[i]), acc[i][j], 0, 0, 0);
+      };
+#pragma unroll
+      for (int st = 0; st < 8; ++st) step(st, xr[st % RING], xr[(st + RING - 1) % RING]);
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        dsc[j] = dsn[j];
+#pragma unroll
+        for (int q = 0; q < QW; ++q) cw[j][q] = cwn[j][q];
+      }
+    }
+  }
+
+  // ---- the eight partial sums, in a fixed order: S_w = P_w + P_{w+4}, then
+  // ((S_0 + S_1) + (S_2 + S_3)).  D[n = 4g + e][m = col] of each 16 x 16
+  // result is out[16 i + col][n0 + 16 j + 4g + e].  The barriers wait for
+  // LDS only: loads still in flight (fragments past the last chunk) are not
+  // waited for here.
+  float4 (*red)[RT * CT][64] = reinterpret_cast<float4 (*)[RT * CT][64]>(smem);
+  if constexpr (LDS_W) lds_barrier();           // every wave is done with the staged weights
+  if (wave >= 4) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CT; ++j)
+        red[wave - 4][i * CT + j][lane] =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+  }
+  lds_barrier();
+  if (wave < 4) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        const float4 o = red[wave][i * CT + j][lane];
+        acc[i][j] += floatx4_t{o.x, o.y, o.z, o.w};
+      }
+  }
+  lds_barrier();
+  if (wave < 4) {
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CT; ++j)
+        red[wave][i * CT + j][lane] =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+  }
+  lds_barrier();
+  const bool vec = (N & 3) == 0;
+  for (int it = tid; it < RT * CT * 64; it += 512) {
+    const int q = it >> 6, l = it & 63;
+    const int i = q / CT, j = q - i * CT;
+    const int m = 16 * i + (l & 15), n = n0 + 16 * j + 4 * (l >> 4);
+    if (m >= M || n >= N) continue;
+    const float4 a = red[0][q][l], b = red[1][q][l], cc = red[2][q][l], d = red[3][q][l];
+    floatx4_t v = {(a.x + b.x) + (cc.x + d.x), (a.y + b.y) + (cc.y + d.y),
+                   (a.z + b.z) + (cc.z + d.z), (a.w + b.w) + (cc.w + d.w)};
+    const size_t o = size_t(m) * uint32_t(N) + uint32_t(n);
+    if (vec && n + 3 < N) {
+      if (residual) {
+        const float4 rr = *reinterpret_cast<const float4*>(residual + o);
+        v = floatx4_t{rr.x + v[0], rr.y + v[1], rr.z + v[2], rr.w + v[3]};
+      }
+      __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t*>(out + o));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e < N) {
+          float r = v[e];
+          if (residual) r = residual[o + e] + r;
+          out[o + e] = r;
+        }
+      }
+    }
+  }
+}
+
+// Workspace bytes of the binary16 x fragments for an M x K call (M <= 128).
+inline size_t ks_workspace_bytes(int64_t m, int64_t k) {
+  const int64_t rt = (m + 15) / 16;
+  const int64_t nch = (k + kChunk - 1) / kChunk;
+  return size_t(rt) * size_t(nch) * 8u * 1024u;
+}
+
+template <int RT, Fmt F>
+hipError_t launch_ks(const uint8_t* soa, const float* x, const float* residual, float* out,
+                     int64_t m, int64_t n, int64_t k, void* ws, hipStream_t stream) {
+  constexpr int CT = 3;
+  const int nch = int((k + kChunk - 1) / kChunk);
+  hipLaunchKernelGGL(x16_fragments_kernel, dim3(unsigned(RT * nch)), dim3(256), 0, stream, x,
+                     int(m), int(k), nch, static_cast<u32x4_t*>(ws));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (n + 16 * CT - 1) / (16 * CT);
+  const size_t so = scales_offset(F, n, k);
+  constexpr int RING = 2;
+  if (F == Fmt::kTq2 && k <= kKsMaxK)
+    hipLaunchKernelGGL((gemm_ks_kernel<RT, CT, RING, F, F == Fmt::kTq2>), dim3(unsigned(blocks)),
+                       dim3(512), 0, stream, soa, soa + so, static_cast<const u32x4_t*>(ws),
+                       residual, out, int(m), int(n), int(k), nch);
+  else
+    hipLaunchKernelGGL((gemm_ks_kernel<RT, CT, RING, F, false>), dim3(unsigned(blocks)),
+                       dim3(512), 0, stream, soa, soa + so, static_cast<const u32x4_t*>(ws),
+                       residual, out, int(m), int(n), int(k), nch);
+  return hipGetLastError();
+}
+
+template <Fmt F>
+hipError_t dispatch_ks(const uint8_t* soa, const float* x, const float* residual, float* out,
+                       int64_t m, int64_t n, int64_t k, void* ws, hipStream_t stream) {
+  switch ((m + 15) / 16) {
+    case 2: return launch_ks<2, F>(soa, x, residual, out, m, n, k, ws, stream);
+    case 3: return launch_ks<3, F>(soa, x, residual, out, m, n, k, ws, stream);
+    case 4: return launch_ks<4, F>(soa, x, residual, out, m, n, k, ws, stream);
+    case 5: return launch_ks<5, F>(soa, x, residual, out, m, n, k, ws, stream);
+    case 6: return launch_ks<6, F>(soa, x, residual, out, m, n, k, ws, stream);
+    case 7: return launch_ks<7, F>(soa, x, residual, out, m, n, k, ws, stream);
+    case 8: return launch_ks<8, F>(soa, x, residual, out, m, n, k, ws, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Skinny variant for M <= 16 with x split into two binary16 limbs (the
 // f32-class path).  At this M the work per weight is tiny, so the kernel is
 // laid out for the weight stream rather than for matrix-core reuse: the
@@ -1875,6 +2249,17 @@ hipError_t launch_gemm_swiglu_q1(int path, const uint8_t* gate, const uint8_t* u
                                  const float* x, float* out, int64_t m, int64_t n, int64_t k,
                                  hipStream_t stream) {
   return dispatch<true, Fmt::kQ1>(path, gate, up, x, nullptr, out, m, n, k, stream);
+}
+
+size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  if (m <= kSplitMaxM || m > kWsMaxM) return 0;
+  return ks_workspace_bytes(m, k);
+}
+
+hipError_t launch_gemm_ws(const uint8_t* soa, const float* x, const float* residual, float* out,
+                          int64_t m, int64_t n, int64_t k, void* ws, hipStream_t stream) {
+  return dispatch_ks<Fmt::kTq2>(soa, x, residual, out, m, n, k, ws, stream);
 }
 
 }  // namespace tq2

@@ -111,4 +111,13 @@ constexpr int64_t kSplitMaxM = 16;
 constexpr int64_t kGemmMaxK = int64_t(1) << 21;
 constexpr int64_t kGemmMaxCodeBytes = int64_t(1) << 31;
 
+// Path 2 with a caller workspace (tq2_gemm_ws) for kSplitMaxM < M <= kWsMaxM:
+// x is written once per call as binary16 MFMA fragments into the workspace
+// (gemm_ws_bytes of them), and a K-split kernel reads them.  gemm_ws_bytes
+// is 0 where tq2_gemm_ws runs tq2_gemm's kernels instead.
+constexpr int64_t kWsMaxM = 128;
+size_t gemm_ws_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_ws(const uint8_t* soa, const float* x, const float* residual, float* out,
+                          int64_t m, int64_t n, int64_t k, void* ws, hipStream_t stream);
+
 }  // namespace tq2

@@ -39,6 +39,8 @@ EXPORTED_SYMBOLS = (
     "tq2_gemv",
     "tq2_gemv_batched",
     "tq2_gemm",
+    "tq2_gemm_workspace_bytes",
+    "tq2_gemm_ws",
     "tq2_gemm_precise",
     "tq2_gate_up_swiglu",
     "tq2_q1_aos_bytes",
@@ -102,6 +104,10 @@ def _load():
     lib.tq2_gemm.restype = c_int
     lib.tq2_gemm_precise.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.tq2_gemm_precise.restype = c_int
+    lib.tq2_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.tq2_gemm_workspace_bytes.restype = sz
+    lib.tq2_gemm_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
+    lib.tq2_gemm_ws.restype = c_int
     lib.tq2_gate_up_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.tq2_gate_up_swiglu.restype = c_int
     lib.tq2_q1_aos_bytes.argtypes = [i64, i64]
@@ -174,6 +180,10 @@ def gemm_path(m: int, n: int, k: int) -> int:
     return int(lib.tq2_gemm_path(m, n, k))
 
 
+def gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib.tq2_gemm_workspace_bytes(m, n, k))
+
+
 def status_string(status: int) -> str:
     return lib.tq2_status_string(status).decode()
 
@@ -203,6 +213,12 @@ def gemm_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, 
              stream: int = 0) -> int:
     return int(lib.tq2_gemm(soa_ptr, x_ptr, residual_ptr or None, out_ptr, m, n, k,
                             stream or None))
+
+
+def gemm_ws_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, n: int, k: int,
+                ws_ptr: int, ws_bytes: int, stream: int = 0) -> int:
+    return int(lib.tq2_gemm_ws(soa_ptr, x_ptr, residual_ptr or None, out_ptr, m, n, k,
+                               ws_ptr or None, ws_bytes, stream or None))
 
 
 def gemm_precise_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, n: int,
@@ -327,10 +343,12 @@ def gemv(soa, x, n: int, k: int, residual=None, out=None, fmt: str = "tq2"):
 
 
 def gemm(soa, x, n: int, k: int, residual=None, out=None, precise: bool = False,
-         fmt: str = "tq2"):
+         fmt: str = "tq2", workspace="auto"):
     """out[m, n] = residual[m, n] + sum_k x[m, k] * w[n, k]; x is f32 [m, k].
     precise=True calls tq2_gemm_precise (f32-class accuracy at every M; TQ2
-    only)."""
+    only).  workspace (TQ2, not precise): "auto" calls tq2_gemm_ws with a
+    workspace allocated here where tq2_gemm_workspace_bytes is nonzero; a
+    uint8 device tensor is used as that workspace; None calls tq2_gemm."""
     torch = _torch()
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x must be [m, %d]" % k)
@@ -345,9 +363,24 @@ def gemm(soa, x, n: int, k: int, residual=None, out=None, precise: bool = False,
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _require(out, torch.float32, m * n, "out")
     dev = _one_device(("x", x), ("soa", soa), ("residual", residual), ("out", out))
+    res_ptr = residual.data_ptr() if residual is not None else 0
+    if fmt == "tq2" and not precise and workspace is not None:
+        need = gemm_workspace_bytes(m, n, k)
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        elif need:
+            if not (isinstance(workspace, torch.Tensor) and workspace.dtype == torch.uint8
+                    and workspace.is_contiguous() and workspace.device == dev):
+                raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+        if need and workspace is not None:
+            _check(_launch(dev, gemm_ws_ptr, soa.data_ptr(), x.data_ptr(), res_ptr,
+                           out.data_ptr(), m, n, k, workspace.data_ptr(), workspace.numel()),
+                   "gemm_ws")
+            return out
     call = q1_gemm_ptr if fmt == "q1" else (gemm_precise_ptr if precise else gemm_ptr)
-    _check(_launch(dev, call, soa.data_ptr(), x.data_ptr(),
-                   residual.data_ptr() if residual is not None else 0, out.data_ptr(), m, n, k),
+    _check(_launch(dev, call, soa.data_ptr(), x.data_ptr(), res_ptr, out.data_ptr(), m, n, k),
            "gemm_precise" if precise else "gemm")
     return out
 

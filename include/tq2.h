@@ -174,6 +174,32 @@ int tq2_gemv_batched(const tq2_gemv_problem* problems, int count, void* stream);
 int tq2_gemm(const void* soa, const float* x, const float* residual, float* out,
              int64_t m, int64_t n, int64_t k, void* stream);
 
+/* Bytes of device workspace that tq2_gemm_ws uses for an (m, n, k) call, or 0
+ * where it uses none (it then runs tq2_gemm's kernels); 0 also for invalid
+ * shapes.  Nonzero for path 2 with M <= 128: about 2 * ceil(M/16) * 16 * K
+ * bytes (x as binary16, rows padded to 16 and K to 256). */
+size_t tq2_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* tq2_gemm with a device workspace from the caller, for path 2 at
+ * 16 < M <= 128.  Same operation, arguments, aliasing rules, tolerance
+ * (path 2's 2e-3 * sum|x w|: x rounded to binary16, weights exact binary16
+ * code * d, f32 accumulation, as in the pages' f16-staged v9/v10 kernels,
+ * oxibonsai-kernels 0.1.5, pipelines.rs, fields `gemm_tq2_g128_v9_simdgroup`
+ * / `gemm_tq2_g128_v10_simdgroup`) and errors as tq2_gemm; the results may
+ * differ from tq2_gemm's in the last bits (another summation order).
+ * x is first written once into `workspace` as binary16 in the matrix cores'
+ * operand order, so the GEMM's blocks read half the bytes of x and need no
+ * staging; each block then splits K over its waves.
+ * workspace: device memory of workspace_bytes >= tq2_gemm_workspace_bytes(
+ * m, n, k), 256-byte aligned, not overlapping soa, x, residual or out; it is
+ * overwritten (owned by the call until the stream reaches its end), so calls
+ * that share one workspace must be ordered (one stream).  Where that size is
+ * 0 the call is tq2_gemm and workspace may be NULL.  Errors: those of
+ * tq2_gemm, and INVALID for a missing or too small workspace, ALIGN, ALIAS. */
+int tq2_gemm_ws(const void* soa, const float* x, const float* residual, float* out,
+                int64_t m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                void* stream);
+
 /* tq2_gemm with f32-class accuracy at every M: the split-binary16 matrix-core
  * kernel of path 1 (x = hi + lo, both parts against the same exact binary16
  * weight, f32 accumulation) for every M >= 2, and the GEMV for M == 1; error

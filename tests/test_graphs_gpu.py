@@ -43,6 +43,7 @@ def test_graph_replays_match_eager(tq2):
         "batched": torch.empty(3, n, device="cuda"),
         "skinny": torch.empty(8, n, device="cuda"),
         "tile": torch.empty(40, n, device="cuda"),
+        "tile_plain": torch.empty(40, n, device="cuda"),
         "precise": torch.empty(40, n, device="cuda"),
         "swiglu1": torch.empty(1, n, device="cuda"),
         "swiglu40": torch.empty(40, n, device="cuda"),
@@ -56,7 +57,8 @@ def test_graph_replays_match_eager(tq2):
         tq2.gemv_batched([dict(soa=soa, x=x[i], n=n, k=k, residual=res[i] if i != 1 else None,
                                out=o["batched"][i]) for i in range(3)])
         tq2.gemm(soa, x[:8], n, k, residual=res[:8], out=o["skinny"])
-        tq2.gemm(soa, x, n, k, residual=res, out=o["tile"])
+        tq2.gemm(soa, x, n, k, residual=res, out=o["tile"])            # tq2_gemm_ws
+        tq2.gemm(soa, x, n, k, residual=res, out=o["tile_plain"], workspace=None)
         tq2.gemm(soa, x, n, k, residual=res, out=o["precise"], precise=True)
         tq2.gate_up_swiglu(soa, soa, x[:1], n, k, out=o["swiglu1"])
         tq2.gate_up_swiglu(soa, soa, x, n, k, out=o["swiglu40"])

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 19
     assert sorted(tq2.EXPORTED_SYMBOLS) == names
     lib = ctypes.CDLL(tq2.LIB_PATH)
     for name in names:
@@ -101,6 +101,37 @@ def test_argument_checks_before_any_device_work():
     assert g(0, 0, 0, 0, 4, 0, 128) == tq2.TQ2_OK
     assert v(0, 0, 0, 0, 0, 128) == tq2.TQ2_OK
     assert r(0, 0, 0, 128) == tq2.TQ2_OK
+
+
+def test_gemm_workspace_sizes_and_checks():
+    """tq2_gemm_workspace_bytes: nonzero exactly on path 2 up to M = 128, x as
+    binary16 with rows padded to 16 and K to 256; tq2_gemm_ws rejects a
+    missing, small, misaligned or overlapping workspace before any device
+    work, and with no workspace needed it is tq2_gemm (same checks)."""
+    wb = tq2.gemm_workspace_bytes
+    for m in (1, 2, 16, 129, 1536):
+        assert wb(m, 11008, 4096) == 0
+    assert wb(17, 64, 128) == 2 * 16 * 256 * 2
+    assert wb(100, 11008, 4096) == 7 * 16 * 4096 * 2
+    assert wb(128, 50, 12416) == 8 * 16 * 12544 * 2
+    assert wb(100, 10, 100) == 0 and wb(-1, 10, 128) == 0 and wb(0, 10, 128) == 0
+    assert wb(40, 16, (1 << 21) + 128) == 0                    # K past the matrix-core limit
+    w = tq2.gemm_ws_ptr
+    X, O, W = A + (1 << 40), A + (2 << 40), A + (3 << 40)
+    need = wb(100, 64, 4096)
+    assert w(A, X, 0, O, 100, 64, 4096, 0, need) == tq2.TQ2_ERR_INVALID
+    assert w(A, X, 0, O, 100, 64, 4096, W, need - 1) == tq2.TQ2_ERR_INVALID
+    assert w(A, X, 0, O, 100, 64, 4096, W + 16, need) == tq2.TQ2_ERR_ALIGN
+    assert w(A, X, 0, O, 100, 64, 4096, X + 256, need) == tq2.TQ2_ERR_ALIAS
+    assert w(A, X, 0, O, 100, 64, 4096, O, need) == tq2.TQ2_ERR_ALIAS
+    assert w(A, X, O + (1 << 30), O, 100, 64, 4096, O + (1 << 30), need) == tq2.TQ2_ERR_ALIAS
+    assert w(A, X, 0, O, 100, 64, 4096, A, need) == tq2.TQ2_ERR_ALIAS
+    assert w(A, X, 0, O, 100, 64, 100, W, need) == tq2.TQ2_ERR_SHAPE
+    assert w(A + 64, X, 0, O, 100, 64, 4096, W, need) == tq2.TQ2_ERR_ALIGN
+    assert w(A, X, 0, X + 16, 100, 64, 4096, W, need) == tq2.TQ2_ERR_ALIAS
+    assert w(0, 0, 0, 0, 0, 64, 4096, 0, 0) == tq2.TQ2_OK
+    # no workspace needed (M <= 16): the tq2_gemm checks, workspace ignored
+    assert w(A, X, 0, X + 16, 8, 64, 4096, 0, 0) == tq2.TQ2_ERR_ALIAS
 
 
 def test_size_limits_before_any_device_work():

@@ -32,7 +32,7 @@ def upload_weight(tq2, aos, n, k):
     return tq2.reformat_aos_to_soa(_dev(aos), n, k)
 
 
-def run_case(tq2, case, force_gemv=False, inplace=False, precise=False):
+def run_case(tq2, case, force_gemv=False, inplace=False, precise=False, workspace="auto"):
     m, n, k = case["m"], case["n"], case["k"]
     soa = upload_weight(tq2, case["aos"], n, k)
     x = _dev(case["x"].reshape(m, k))
@@ -44,7 +44,8 @@ def run_case(tq2, case, force_gemv=False, inplace=False, precise=False):
         y = tq2.gemv(soa, x.reshape(-1), n, k, residual=None if res_arg is None else res_arg.reshape(-1),
                      out=None if out is None else out.reshape(-1))
     else:
-        y = tq2.gemm(soa, x, n, k, residual=res_arg, out=out, precise=precise)
+        y = tq2.gemm(soa, x, n, k, residual=res_arg, out=out, precise=precise,
+                     workspace=workspace)
     torch.cuda.synchronize()
     return y.cpu().numpy().reshape(m, n)
 
@@ -136,6 +137,8 @@ def test_config2_gemv_residual(tq2):
 @pytest.mark.parametrize("m", [7, 8, 9, 100])
 def test_config3_gemm(tq2, m):
     assert_case(tq2, G.config3(m))
+    if m > 16:
+        assert_case(tq2, G.config3(m), workspace=None)
 
 
 def test_config4_gemm(tq2):
@@ -610,6 +613,58 @@ def test_swiglu_gemm_shapes(tq2, m, n, k):
 def test_tile_heights(tq2, m):
     c = G.random_case(9200 + m, m, 150, 640, residual=(m % 2 == 0))
     assert_case(tq2, c)
+
+
+# tq2_gemm_ws (16 < M <= 128): tq2.gemm uses it by default; the same shapes
+# through tq2_gemm itself (no workspace) keep the warp-specialised kernel
+# covered.  K <= 12288 stages the block's weights in LDS (K = 12288 fills
+# it); K = 12416 and 16640 take the per-chunk weight loads.
+WS_SHAPES = [(17, 200, 384), (31, 33, 128), (32, 300, 512), (33, 100, 256), (64, 129, 384),
+             (65, 64, 1024), (96, 192, 256), (97, 250, 640), (100, 90, 12416), (104, 70, 4096),
+             (105, 49, 1152), (128, 300, 512), (33, 70, 16640), (77, 100, 12288)]
+
+
+@pytest.mark.parametrize("m,n,k", WS_SHAPES)
+def test_path2_with_and_without_workspace(tq2, m, n, k):
+    c = G.random_case(2500 + m + n + k, m, n, k, residual=(m % 2 == 1))
+    assert tq2.gemm_workspace_bytes(m, n, k) > 0
+    a = assert_case(tq2, c)                          # tq2_gemm_ws
+    b = assert_case(tq2, c, workspace=None)          # tq2_gemm
+    assert a.shape == b.shape
+
+
+def test_workspace_contents_do_not_matter(tq2):
+    """The pre-pass writes every workspace byte the GEMM reads (rows past M
+    and k past K as zeros): a workspace full of binary16 NaNs beforehand, and
+    one reused by a second, smaller call, give the oracle's results."""
+    m, n, k = 100, 130, 1152
+    need = tq2.gemm_workspace_bytes(m, n, k)
+    ws = torch.full((need + 4096,), 0xFF, dtype=torch.uint8, device="cuda")
+    for mm, kk in ((m, k), (37, 640)):
+        c = G.random_case(2600 + mm, mm, n, kk, residual=True)
+        soa = upload_weight(tq2, c["aos"], n, kk)
+        x = _dev(c["x"].reshape(mm, kk))
+        res = _dev(c["residual"].reshape(mm, n))
+        y = tq2.gemm(soa, x, n, kk, residual=res, workspace=ws)
+        torch.cuda.synchronize()
+        ref, sc = oracle_full(c)
+        ok, msg = check(y.cpu().numpy(), ref, sc, 2, c["name"] + "_ws")
+        print(msg, flush=True)
+        assert ok, msg
+        assert np.isfinite(y.cpu().numpy()).all()
+
+
+def test_workspace_in_place_residual_and_repeat(tq2):
+    """In-place residual through tq2_gemm_ws, and two calls on the same
+    inputs give identical bits (fixed reduction order)."""
+    c = G.random_case(2700, 100, 96, 4096, residual=True)
+    assert_case(tq2, c, inplace=True)
+    soa = upload_weight(tq2, c["aos"], 96, 4096)
+    x = _dev(c["x"].reshape(100, 4096))
+    y1 = tq2.gemm(soa, x, 96, 4096)
+    y2 = tq2.gemm(soa, x, 96, 4096)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
 
 
 @pytest.mark.parametrize("m", [17, 33, 49, 81, 105, 128])
