@@ -16,6 +16,24 @@ constexpr int kMaxDevices = 64;
 // 0 = unknown, 1 = gfx950, 2 = other architecture.
 std::atomic<int> g_device_kind[kMaxDevices];
 
+// Device memory of tq2_gemm_noalloc: one fixed array per GPU, held from the
+// library's load until the process ends, so that call allocates nothing.
+// In host code `scratch` is only the host-side stand-in of the symbol, not a
+// device address: device_scratch() returns the address on the current
+// device (hipGetSymbolAddress, once per device), and only that is passed on.
+static __device__ __align__(256) uint8_t scratch[TQ2_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The scratch array's address on device `dev` (current), or nullptr.
+void* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TQ2_ERR_DEVICE;
@@ -279,6 +297,26 @@ int tq2_gemm_ws(const void* soa, const float* x, const float* residual, float* o
   if (st != TQ2_OK) return st;
   return launch_status(tq2::launch_gemm_ws(static_cast<const uint8_t*>(soa), x, residual, out, m,
                                            n, k, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int tq2_gemm_noalloc(const void* soa, const float* x, const float* residual, float* out,
+                     int64_t m, int64_t n, int64_t k, void* stream) {
+  int st = check_shape(m, n, k);
+  if (st != TQ2_OK) return st;
+  if (m == 0 || n == 0) return TQ2_OK;
+  const size_t need = tq2_gemm_workspace_bytes(m, n, k);
+  if (need == 0) return tq2_gemm(soa, x, residual, out, m, n, k, stream);
+  if (need > size_t(TQ2_NOALLOC_SCRATCH_BYTES)) return TQ2_ERR_INVALID;
+  st = check_matmul_host(soa, x, residual, out, m, n, k);
+  if (st != TQ2_OK) return st;
+  st = check_device();
+  if (st != TQ2_OK) return st;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ2_ERR_DEVICE;
+  void* ws = device_scratch(dev);
+  if (!ws) return TQ2_ERR_DEVICE;
+  return launch_status(tq2::launch_gemm_ws(static_cast<const uint8_t*>(soa), x, residual, out, m,
+                                           n, k, ws, static_cast<hipStream_t>(stream)));
 }
 
 int tq2_gemm_precise(const void* soa, const float* x, const float* residual, float* out,

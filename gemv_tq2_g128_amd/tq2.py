@@ -24,6 +24,7 @@ TQ2_ERR_ALIGN = -3
 TQ2_ERR_ALIAS = -4
 TQ2_ERR_DEVICE = -5
 TQ2_ERR_LAUNCH = -6
+NOALLOC_SCRATCH_BYTES = 4 << 20   # TQ2_NOALLOC_SCRATCH_BYTES (include/tq2.h)
 
 GEMV_BATCH_MAX = 32
 
@@ -41,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "tq2_gemm",
     "tq2_gemm_workspace_bytes",
     "tq2_gemm_ws",
+    "tq2_gemm_noalloc",
     "tq2_gemm_precise",
     "tq2_gate_up_swiglu",
     "tq2_q1_aos_bytes",
@@ -108,6 +110,8 @@ def _load():
     lib.tq2_gemm_workspace_bytes.restype = sz
     lib.tq2_gemm_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
     lib.tq2_gemm_ws.restype = c_int
+    lib.tq2_gemm_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.tq2_gemm_noalloc.restype = c_int
     lib.tq2_gate_up_swiglu.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.tq2_gate_up_swiglu.restype = c_int
     lib.tq2_q1_aos_bytes.argtypes = [i64, i64]
@@ -219,6 +223,12 @@ def gemm_ws_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: in
                 ws_ptr: int, ws_bytes: int, stream: int = 0) -> int:
     return int(lib.tq2_gemm_ws(soa_ptr, x_ptr, residual_ptr or None, out_ptr, m, n, k,
                                ws_ptr or None, ws_bytes, stream or None))
+
+
+def gemm_noalloc_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, n: int,
+                     k: int, stream: int = 0) -> int:
+    return int(lib.tq2_gemm_noalloc(soa_ptr, x_ptr, residual_ptr or None, out_ptr, m, n, k,
+                                    stream or None))
 
 
 def gemm_precise_ptr(soa_ptr: int, x_ptr: int, residual_ptr: int, out_ptr: int, m: int, n: int,

@@ -200,6 +200,25 @@ int tq2_gemm_ws(const void* soa, const float* x, const float* residual, float* o
                 int64_t m, int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/* Size of the device array behind tq2_gemm_noalloc (4 MiB per GPU). */
+#define TQ2_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+/* tq2_gemm_ws without a workspace argument, for callers that cannot allocate
+ * device memory at all: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The workspace is a fixed array of
+ * TQ2_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * library's load until the process ends; the call allocates and frees
+ * nothing.  Same operation, arguments, rules, tolerance and errors as
+ * tq2_gemm_ws, and the same results bit for bit.  Limit: a call whose
+ * tq2_gemm_workspace_bytes(m, n, k) exceeds TQ2_NOALLOC_SCRATCH_BYTES
+ * returns TQ2_ERR_INVALID and enqueues nothing (at M = 100 that is
+ * K > 18688; at M = 128, K > 16384); where that size is 0 the call is
+ * tq2_gemm.  Every call on one GPU shares that GPU's array, so calls that
+ * overlap on one GPU (concurrent streams, or graph replays in flight
+ * together) race and may return wrong results; order them on one stream. */
+int tq2_gemm_noalloc(const void* soa, const float* x, const float* residual, float* out,
+                     int64_t m, int64_t n, int64_t k, void* stream);
+
 /* tq2_gemm with f32-class accuracy at every M: the split-binary16 matrix-core
  * kernel of path 1 (x = hi + lo, both parts against the same exact binary16
  * weight, f32 accumulation) for every M >= 2, and the GEMV for M == 1; error

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     assert sorted(tq2.EXPORTED_SYMBOLS) == names
     lib = ctypes.CDLL(tq2.LIB_PATH)
     for name in names:
@@ -132,6 +132,28 @@ def test_gemm_workspace_sizes_and_checks():
     assert w(0, 0, 0, 0, 0, 64, 4096, 0, 0) == tq2.TQ2_OK
     # no workspace needed (M <= 16): the tq2_gemm checks, workspace ignored
     assert w(A, X, 0, X + 16, 8, 64, 4096, 0, 0) == tq2.TQ2_ERR_ALIAS
+
+
+def test_noalloc_limits_before_any_device_work():
+    """tq2_gemm_noalloc: the scratch size in the header is the binding's, a
+    call that needs more workspace than it holds is INVALID before any
+    device work, and the usual checks come first where they apply."""
+    with open(os.path.join(ROOT, "include", "tq2.h")) as f:
+        text = f.read()
+    val = re.search(r"#define\s+TQ2_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert int(val.group(1)) << int(val.group(2)) == tq2.NOALLOC_SCRATCH_BYTES
+    na = tq2.gemm_noalloc_ptr
+    X, O = A + (1 << 40), A + (2 << 40)
+    wb = tq2.gemm_workspace_bytes
+    assert wb(100, 64, 18688) <= tq2.NOALLOC_SCRATCH_BYTES < wb(100, 64, 18944)
+    assert wb(128, 64, 16384) <= tq2.NOALLOC_SCRATCH_BYTES < wb(128, 64, 16640)
+    assert na(A, X, 0, O, 100, 64, 18944) == tq2.TQ2_ERR_INVALID
+    assert na(A, X, 0, O, 128, 64, 16640) == tq2.TQ2_ERR_INVALID
+    assert na(A, X, 0, O, 100, 64, 100) == tq2.TQ2_ERR_SHAPE
+    assert na(A + 64, X, 0, O, 100, 64, 4096) == tq2.TQ2_ERR_ALIGN
+    assert na(A, X, 0, X + 16, 100, 64, 4096) == tq2.TQ2_ERR_ALIAS
+    assert na(A, X, 0, X + 16, 8, 64, 4096) == tq2.TQ2_ERR_ALIAS       # M <= 16: tq2_gemm
+    assert na(0, 0, 0, 0, 0, 64, 4096) == tq2.TQ2_OK
 
 
 def test_size_limits_before_any_device_work():
