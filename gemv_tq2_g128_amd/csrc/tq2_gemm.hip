@@ -1136,7 +1136,9 @@ __global__ __launch_bounds__(512) void gemm_ks_kernel(
   if constexpr (LDS_W) {
     // The block's weight slice into LDS: 16-byte units u = (column jn, unit
     // t16 = 4 c + g of its row), 8 loads in flight per thread, columns past
-    // N read as zeros.
+    // N read as zeros.  The weight is read once per call: its loads carry
+    // the streaming hint, so that they do not push the x fragments out of
+    // the caches.
     const int live_cols = min(NO, N - n0);
     const rsrc_t rcb = make_rsrc(codes + size_t(n0) * row_bytes, uint32_t(live_cols) * row_bytes);
     const rsrc_t rsb = make_rsrc(scales + size_t(n0) * uint32_t(KB) * 2u,
@@ -1151,7 +1153,7 @@ __global__ __launch_bounds__(512) void gemm_ks_kernel(
         const int u = base + q * 512 + tid;
         const int jn = u / upc, t16 = u - jn * upc;
         const uint32_t off = u < units ? uint32_t(jn) * row_bytes + 16u * uint32_t(t16) : 0xFFFFFFF0u;
-        v[q] = __builtin_amdgcn_raw_buffer_load_b128(rcb, off, 0, 0);
+        v[q] = __builtin_amdgcn_raw_buffer_load_b128(rcb, off, 0, kStreamOnce);
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -1164,7 +1166,7 @@ __global__ __launch_bounds__(512) void gemm_ks_kernel(
     }
     uint16_t* sls = reinterpret_cast<uint16_t*>(smem + size_t(nch) * CT * 1024);
     for (int u = tid; u < NO * KB; u += 512)
-      sls[u] = __builtin_amdgcn_raw_buffer_load_b16(rsb, 2u * uint32_t(u), 0, 0);
+      sls[u] = __builtin_amdgcn_raw_buffer_load_b16(rsb, 2u * uint32_t(u), 0, kStreamOnce);
     lds_barrier();
   }
 
