@@ -1075,16 +1075,22 @@ __global__ __launch_bounds__(512) void gemm_ks_kernel(
 
   typedef uint32_t codes_t[QW];
   const uint32_t row_bytes = uint32_t(K / 8) * uint32_t(BITS);
-  const rsrc_t rx = make_rsrc(frag, uint32_t(RT) * uint32_t(nch) * 8u * 1024u);
+  // One resource per row tile (its nch * 8 fragments), so that a step's RT
+  // loads share one per-lane offset and the step's place inside its half
+  // chunk goes into the instructions' immediate offsets.  Fragment loads past
+  // the wave's (or the matrix's) last chunk are issued anyway: they read
+  // another wave's data or, past the row tile's end, zeros (range check),
+  // and keep every load unconditional.
   const uint32_t xrt = uint32_t(nch) * 8u * 1024u;     // bytes per row tile
-  // Fragment loads past the wave's (or the matrix's) last chunk are issued
-  // anyway: they read another wave's data or, past the end, zeros (range
-  // check), and keep every load unconditional.
+  rsrc_t rx[RT];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+    rx[i] = make_rsrc(reinterpret_cast<const uint8_t*>(frag) + size_t(i) * xrt, xrt);
   auto load_x = [&](int c, int st, u32x4_t (&xf)[RT]) {
+    const uint32_t off = uint32_t((c * 8 + (st & 4)) * 1024) + 16u * uint32_t(lane);
 #pragma unroll
     for (int i = 0; i < RT; ++i)
-      xf[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          rx, uint32_t(i) * xrt + uint32_t((c * 8 + st) * 1024) + 16u * uint32_t(lane), 0, 0);
+      xf[i] = __builtin_amdgcn_raw_buffer_load_b128(rx[i], off + uint32_t((st & 3) * 1024), 0, 0);
   };
 
   // Staged weights: wl[(c * CT + j) * 64 + lane] holds the four code words
@@ -1178,13 +1184,18 @@ __global__ __launch_bounds__(512) void gemm_ks_kernel(
 
   const uint32_t magic = 0x64006400u;
   if (c0 < c1) {
+    // Global weights: loaded a chunk ahead (cw / dsc for chunk c, cwn / dsn
+    // for c + 1).  Staged weights: read from LDS at the start of each chunk.
     codes_t cw[CT];
     uint32_t dsc[CT];
-    load_w(c0, cw, dsc);
+    if constexpr (!LDS_W) load_w(c0, cw, dsc);
     for (int c = c0; c < c1; ++c) {
       codes_t cwn[CT];
       uint32_t dsn[CT];
-      load_w(c + 1, cwn, dsn);
+      if constexpr (LDS_W)
+        load_w(c, cw, dsc);
+      else
+        load_w(c + 1, cwn, dsn);
       __builtin_amdgcn_sched_barrier(0);
       // binary16 pair (d, d), or (0, 0) where k runs past K in the last
       // chunk (Q1: the |d| pair, and the words folded by the sign of d).
@@ -1236,11 +1247,13 @@ __global__ __launch_bounds__(512) void gemm_ks_kernel(
       };
 #pragma unroll
       for (int st = 0; st < 8; ++st) step(st, xr[st % RING], xr[(st + RING - 1) % RING]);
+      if constexpr (!LDS_W) {
 #pragma unroll
-      for (int j = 0; j < CT; ++j) {
-        dsc[j] = dsn[j];
+        for (int j = 0; j < CT; ++j) {
+          dsc[j] = dsn[j];
 #pragma unroll
-        for (int q = 0; q < QW; ++q) cw[j][q] = cwn[j][q];
+          for (int q = 0; q < QW; ++q) cw[j][q] = cwn[j][q];
+        }
       }
     }
   }
